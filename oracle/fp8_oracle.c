@@ -1,0 +1,241 @@
+/*
+ * CPU oracle for the unified-FP8 (W8A8) linear layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This library is the slow, plain reference the
+ * HIP path is checked against.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load it; the product path never does.  It
+ * shares no code, headers, tables or constants with the HIP library.
+ *
+ * Sources (web pages on FP8 LLM inference; cited by page and section):
+ *   [DSV4]  "DeepSeek V4 950: unified low-precision dataflow" (2kiu.com),
+ *           §1.2 (decode is bandwidth bound), §2.1 (E4M3 vs E5M2),
+ *           §2.3 (FP8 in, FP32 accumulate), §2.4 (per-channel weight and
+ *           per-token activation scales), §3.1 (scales computed on the fly).
+ *   [L3]    "Llama 3 FP8 deployment and long context" (dpshk.com),
+ *           §1.1 (E4M3 largest value 448, smallest non-zero 2^-9),
+ *           §3.1 (weight-conversion snippet: per-output-channel absmax/448,
+ *           clamped below at 1e-12, cast to float8_e4m3fn),
+ *           §4.1 (scan quantized tensors for NaN/Inf).
+ *   [DEPLOY] "FP8 mixed-precision inference deployment" (ybb.press),
+ *           §1.1 (E4M3 range +-448), §2.3 (clamp to +-448).
+ *
+ * Readings where the pages leave a step open (all float arithmetic below is
+ * IEEE binary32/binary64 with round-to-nearest-even; build without
+ * fast-math and without FP contraction):
+ *   - E4M3 is the OCP "fn" variant: bias 7, no infinities, S.1111.111 is NaN,
+ *     largest finite S.1111.110 = 448, smallest subnormal 2^-9.
+ *   - Encoding rounds to nearest, ties to the even code, and saturates to
+ *     +-448 (infinities included); NaN keeps its sign as S.1111.111.
+ *   - The scale is the dequantization multiplier s = max(fl32(amax/448), 1e-12f)
+ *     for activation rows and weight rows alike; codes are enc(fl32(x / s))
+ *     with a correctly rounded division.
+ *   - The GEMM is sum_k dec(a)*dec(w) accumulated in binary64, which is exact
+ *     here (every product is a multiple of 2^-18 and |sum| < 2^35 for
+ *     K <= 28672), times (double)s_tok * (double)s_ch.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ---------------------------------------------------------------- codec -- */
+
+/* Value of an E4M3 code ([L3] §1.1; [DSV4] §2.1): sign s, exponent field E
+ * (4 bits, bias 7), mantissa field m (3 bits).  E = 0 is subnormal m * 2^-9. */
+double oracle_e4m3_decode(uint8_t code) {
+    int s = (code >> 7) & 1;
+    int E = (code >> 3) & 15;
+    int m = code & 7;
+    double mag;
+    if (E == 15 && m == 7) return NAN;
+    if (E == 0)
+        mag = ldexp((double)m, -9);
+    else
+        mag = ldexp(1.0 + (double)m / 8.0, E - 7);
+    return s ? -mag : mag;
+}
+
+/* Round a non-negative double to an integer, ties to even. */
+static double round_half_even(double q) {
+    double f = floor(q);
+    double d = q - f;
+    if (d > 0.5) return f + 1.0;
+    if (d < 0.5) return f;
+    return (fmod(f, 2.0) == 0.0) ? f : f + 1.0;
+}
+
+/* fp32 -> E4M3 code: round to nearest even on the E4M3 grid, saturate to
+ * +-448 ([DEPLOY] §2.3 clamp), NaN -> S.1111.111. */
+uint8_t oracle_e4m3_encode(float v) {
+    uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    if (isnan(v)) return (uint8_t)(sign | 0x7F);
+    double a = fabs((double)v);
+    if (a >= 448.0) return (uint8_t)(sign | 0x7E);
+    if (a == 0.0) return sign;
+    int e2;
+    frexp(a, &e2);          /* a = f * 2^e2, f in [0.5, 1) */
+    int ex = e2 - 1;        /* a in [2^ex, 2^(ex+1)) */
+    if (ex < -6) {
+        /* below the smallest normal 2^-6: grid step 2^-9, codes 0..8
+           (8 * 2^-9 = 2^-6 is code 0x08, the smallest normal) */
+        double r = round_half_even(ldexp(a, 9));
+        return (uint8_t)(sign | (int)r);
+    }
+    /* binade [2^ex, 2^(ex+1)): 8 steps of 2^(ex-3) */
+    double r = round_half_even(ldexp(a, 3 - ex)); /* in [8, 16] */
+    if (r == 16.0) { ex += 1; r = 8.0; }
+    int E = ex + 7, m = (int)r - 8;
+    return (uint8_t)(sign | (E << 3) | m);
+}
+
+/* ------------------------------------------------------------ quantizer -- */
+
+/* Per-row absmax quantization, the [L3] §3.1 conversion applied to any
+ * row-major matrix: rows of W (per output channel) or rows of X (per token,
+ * computed on the fly as [DSV4] §2.4 and §3.1 describe).
+ *   scale[r] = max(fl32(max_k |x[r,k]|) / 448), 1e-12f)
+ *   q[r,k]   = enc(fl32(x[r,k] / scale[r]))                                 */
+void oracle_quantize_rows(const float* x, int64_t rows, int64_t K, int64_t ldx,
+                          uint8_t* q, int64_t ldq, float* scales) {
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t r = 0; r < rows; ++r) {
+        const float* xr = x + r * ldx;
+        float amax = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            float a = fabsf(xr[k]);
+            if (a > amax) amax = a;
+        }
+        float s = amax / 448.0f;
+        if (s < 1e-12f) s = 1e-12f;
+        scales[r] = s;
+        for (int64_t k = 0; k < K; ++k) {
+            float t = xr[k] / s;
+            q[r * ldq + k] = oracle_e4m3_encode(t);
+        }
+    }
+}
+
+/* --------------------------------------------------------------- GEMM ---- */
+
+static double g_dec[256];
+static int g_dec_ready = 0;
+
+static void dec_table(void) {
+    if (g_dec_ready) return;
+    for (int c = 0; c < 256; ++c) g_dec[c] = oracle_e4m3_decode((uint8_t)c);
+    g_dec_ready = 1;
+}
+
+void oracle_init(void) { dec_table(); }
+
+/* One output element of the scaled FP8 GEMM ([DSV4] §2.3: FP8 operands,
+ * wide accumulation; scales of §2.4 applied after the sum):
+ *   D = sum_k dec(a[k]) * dec(w[k])        (binary64, exact)
+ *   A = sum_k |dec(a[k]) * dec(w[k])|
+ *   ref = D * (s_tok * s_ch),  absref = A * (s_tok * s_ch)                    */
+static void dot_one(const uint8_t* a, const uint8_t* w, int64_t K, double st, double sc,
+                    double* ref, double* absref) {
+    double D = 0.0, A = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+        double p = g_dec[a[k]] * g_dec[w[k]];
+        D += p;
+        A += fabs(p);
+    }
+    double s = st * sc;
+    *ref = D * s;
+    *absref = A * s;
+}
+
+/* Full reference: ref[m,n], absref[m,n] for qa [M,K] (lda), qw [N,K] (ldw). */
+void oracle_gemm_ref(const uint8_t* qa, int64_t lda, const float* s_tok,
+                     const uint8_t* qw, int64_t ldw, const float* s_ch,
+                     int64_t M, int64_t N, int64_t K, double* ref, double* absref) {
+    dec_table();
+#pragma omp parallel for schedule(dynamic, 1) collapse(2)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n)
+            dot_one(qa + m * lda, qw + n * ldw, K, (double)s_tok[m], (double)s_ch[n],
+                    ref + m * N + n, absref + m * N + n);
+}
+
+/* Reference at the listed (m, n) pairs only. */
+void oracle_gemm_ref_sampled(const uint8_t* qa, int64_t lda, const float* s_tok,
+                             const uint8_t* qw, int64_t ldw, const float* s_ch, int64_t K,
+                             const int64_t* ms, const int64_t* ns, int64_t count,
+                             double* ref, double* absref) {
+    dec_table();
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < count; ++i)
+        dot_one(qa + ms[i] * lda, qw + ns[i] * ldw, K, (double)s_tok[ms[i]], (double)s_ch[ns[i]],
+                ref + i, absref + i);
+}
+
+/* Grouped (MoE) reference ([DSV4] §2.3 item 5 and §2.4: experts run in FP8
+ * with per-channel weight scales of their own).  Routed row r belongs to the
+ * expert e with offsets[e] <= r < offsets[e+1]; it reads token row_token[r]:
+ *   y[r,n] = (sum_k dec(qa[tok,k]) * dec(qw[e,n,k])) * s_tok[tok] * s_ch[e,n]
+ * Evaluated at the listed (r, n) pairs.  Returns -1 if a row has no expert. */
+int oracle_grouped_ref_sampled(const uint8_t* qa, const float* s_tok, const int32_t* row_token,
+                               const int32_t* offsets, int64_t E, const uint8_t* qw,
+                               const float* s_ch, int64_t N, int64_t K,
+                               const int64_t* rs, const int64_t* ns, int64_t count,
+                               double* ref, double* absref) {
+    dec_table();
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t i = 0; i < count; ++i) {
+        int64_t r = rs[i], e = -1;
+        for (int64_t j = 0; j < E; ++j)
+            if (offsets[j] <= r && r < offsets[j + 1]) { e = j; break; }
+        if (e < 0) { bad = 1; ref[i] = NAN; absref[i] = NAN; continue; }
+        int64_t t = row_token[r];
+        dot_one(qa + t * K, qw + (e * N + ns[i]) * K, K, (double)s_tok[t],
+                (double)s_ch[e * N + ns[i]], ref + i, absref + i);
+    }
+    return bad ? -1 : 0;
+}
+
+/* ----------------------------------------------------------- BF16 -------- */
+
+/* Nearest bfloat16 (1-8-7 format) of a double, ties to even, as bits.  Used
+ * only to report how many GPU outputs equal the correctly rounded reference. */
+uint16_t oracle_bf16_from_double(double v) {
+    uint16_t sign = signbit(v) ? 0x8000 : 0;
+    if (isnan(v)) return (uint16_t)(sign | 0x7FC0);
+    double a = fabs(v);
+    if (a == 0.0) return sign;
+    int e2;
+    frexp(a, &e2);
+    int ex = e2 - 1;
+    if (ex < -126) ex = -126;                 /* subnormal range: fixed step */
+    double r = round_half_even(ldexp(a, 7 - ex));
+    double mag = ldexp(r, ex - 7);
+    if (mag >= ldexp(1.0, 128)) return (uint16_t)(sign | 0x7F80);
+    float f = (float)mag;                     /* exact: mag has <= 8 significant bits */
+    uint32_t bits;
+    memcpy(&bits, &f, 4);
+    return (uint16_t)(sign | (bits >> 16));
+}
+
+void oracle_bf16_from_double_array(const double* v, int64_t n, uint16_t* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_bf16_from_double(v[i]);
+}
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
