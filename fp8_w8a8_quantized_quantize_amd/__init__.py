@@ -1,0 +1,207 @@
+"""MI355X-native unified-FP8 (W8A8) linear layer: Python binding.
+
+A thin ctypes layer over libfp8w8a8.so (C ABI: include/fp8w8a8.h).  It only
+marshals arguments -- torch tensors become device pointers, strides and the
+current HIP stream -- and turns status codes into exceptions.  Every step of
+the computation runs in the library's gfx950 kernels; there is no fallback:
+if the library is missing, importing a function raises.
+
+Entry points (same names as the C ABI):
+  fp8_quantize_per_token(x)                -> (q uint8 [M,K], scales fp32 [M])
+  fp8_gemm_scaled(qa, s_tok, qw, s_ch)     -> y bf16 [M,N]
+  fp8_quant_gemm_fused(x, qw, s_ch)        -> y bf16 [M,N]  (optionally qa, s_tok)
+  fp8_gemm_grouped_scaled(qa, s_tok, row_token, expert_offsets, qw, s_ch) -> y bf16 [R,N]
+  fp8_workspace_bytes(M, N, K), fp8_grouped_workspace_bytes(T, R, E, N, K)
+  fp8_status_string(code)
+"""
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfp8w8a8.so")
+
+FP8_OK = 0
+FP8_ERR_INVALID_ARGUMENT = 1
+FP8_ERR_UNSUPPORTED = 2
+FP8_ERR_WORKSPACE = 3
+FP8_ERR_DEVICE = 4
+
+# exported symbols, as declared in include/fp8w8a8.h
+EXPORTS = ("fp8_quantize_per_token", "fp8_gemm_scaled", "fp8_quant_gemm_fused", "fp8_gemm_grouped_scaled",
+           "fp8_workspace_bytes", "fp8_grouped_workspace_bytes", "fp8_status_string")
+
+_lib = None
+
+
+class Fp8Error(RuntimeError):
+    def __init__(self, fn, code):
+        self.code = code
+        super().__init__(f"{fn} failed: {status_name(code)}")
+
+
+def lib():
+    """Load libfp8w8a8.so (raises if it was not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run __graft_entry__.build() "
+                               "(or python fp8_w8a8_quantized_quantize_amd/_build.py)")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, vp, sz, st = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+        L.fp8_quantize_per_token.restype = st
+        L.fp8_quantize_per_token.argtypes = [vp, i64, i64, i64, vp, i64, vp, vp]
+        L.fp8_gemm_scaled.restype = st
+        L.fp8_gemm_scaled.argtypes = [vp, i64, vp, vp, i64, vp, vp, i64, i64, i64, i64, vp, sz, vp]
+        L.fp8_quant_gemm_fused.restype = st
+        L.fp8_quant_gemm_fused.argtypes = [vp, i64, vp, i64, vp, vp, i64, i64, i64, i64, vp, vp, vp, sz, vp]
+        L.fp8_gemm_grouped_scaled.restype = st
+        L.fp8_gemm_grouped_scaled.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, sz, vp]
+        L.fp8_workspace_bytes.restype = sz
+        L.fp8_workspace_bytes.argtypes = [i64, i64, i64]
+        L.fp8_grouped_workspace_bytes.restype = sz
+        L.fp8_grouped_workspace_bytes.argtypes = [i64, i64, i64, i64, i64]
+        L.fp8_status_string.restype = ctypes.c_char_p
+        L.fp8_status_string.argtypes = [st]
+        _lib = L
+    return _lib
+
+
+def status_name(code):
+    return lib().fp8_status_string(int(code)).decode()
+
+
+def _check(fn, code):
+    if code != FP8_OK:
+        raise Fp8Error(fn, code)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _rows(t, dtype, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or not t.is_cuda:
+        raise TypeError(f"{name}: expected a {dtype} CUDA tensor")
+    if t.dim() != 2 or (t.shape[0] > 0 and t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError(f"{name}: expected a 2-D row-major tensor (unit stride along the last dim)")
+    return t.shape[0], t.shape[1], (t.stride(0) if t.shape[0] > 1 else t.shape[1])
+
+
+def _vec(t, dtype, name, n):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or not t.is_cuda or not t.is_contiguous():
+        raise TypeError(f"{name}: expected a contiguous {dtype} CUDA tensor")
+    if t.numel() != n:
+        raise ValueError(f"{name}: expected {n} elements, got {t.numel()}")
+
+
+def fp8_workspace_bytes(M, N, K):
+    return int(lib().fp8_workspace_bytes(M, N, K))
+
+
+def fp8_grouped_workspace_bytes(T, R, E, N, K):
+    return int(lib().fp8_grouped_workspace_bytes(T, R, E, N, K))
+
+
+def fp8_status_string(code):
+    return status_name(code)
+
+
+def fp8_quantize_per_token(x, q=None, scales=None, stream=None):
+    """Per-row absmax E4M3 quantization of fp32 x [M, K] -> (q uint8 [M, K], scales fp32 [M])."""
+    torch = _torch()
+    M, K, ldx = _rows(x, torch.float32, "x")
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(M, dtype=torch.float32, device=x.device)
+    _, _, ldq = _rows(q, torch.uint8, "q")
+    _vec(scales, torch.float32, "scales", M)
+    _check("fp8_quantize_per_token",
+           lib().fp8_quantize_per_token(_ptr(x), M, K, ldx, _ptr(q), ldq, _ptr(scales), _stream(stream)))
+    return q, scales
+
+
+def fp8_gemm_scaled(qa, s_tok, qw, s_ch, y=None, ws=None, stream=None):
+    """y[m,n] = bf16(sum_k e4m3(qa[m,k]) e4m3(qw[n,k]) * s_tok[m] * s_ch[n])."""
+    torch = _torch()
+    M, K, lda = _rows(qa, torch.uint8, "qa")
+    N, K2, ldw = _rows(qw, torch.uint8, "qw")
+    if K2 != K:
+        raise ValueError("qa and qw disagree on K")
+    _vec(s_tok, torch.float32, "s_tok", M)
+    _vec(s_ch, torch.float32, "s_ch", N)
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=qa.device)
+    _, _, ldy = _rows(y, torch.bfloat16, "y")
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check("fp8_gemm_scaled",
+           lib().fp8_gemm_scaled(_ptr(qa), lda, _ptr(s_tok), _ptr(qw), ldw, _ptr(s_ch), _ptr(y), ldy, M, N, K,
+                                 _ptr(ws), ws_bytes, _stream(stream)))
+    return y
+
+
+def fp8_quant_gemm_fused(x, qw, s_ch, y=None, qa_out=None, s_tok_out=None, ws=None, stream=None):
+    """Quantize x per token, then the scaled FP8 GEMM, in one call -> y bf16 [M, N]."""
+    torch = _torch()
+    M, K, ldx = _rows(x, torch.float32, "x")
+    N, K2, ldw = _rows(qw, torch.uint8, "qw")
+    if K2 != K:
+        raise ValueError("x and qw disagree on K")
+    _vec(s_ch, torch.float32, "s_ch", N)
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _, _, ldy = _rows(y, torch.bfloat16, "y")
+    if qa_out is not None:
+        if qa_out.dtype != torch.uint8 or tuple(qa_out.shape) != (M, K) or not qa_out.is_contiguous():
+            raise ValueError("qa_out: expected a contiguous uint8 [M, K] tensor")
+    if s_tok_out is not None:
+        _vec(s_tok_out, torch.float32, "s_tok_out", M)
+    need = fp8_workspace_bytes(M, N, K)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    ws_bytes = ws.numel() * ws.element_size()
+    _check("fp8_quant_gemm_fused",
+           lib().fp8_quant_gemm_fused(_ptr(x), ldx, _ptr(qw), ldw, _ptr(s_ch), _ptr(y), ldy, M, N, K,
+                                      _ptr(qa_out), _ptr(s_tok_out), _ptr(ws), ws_bytes, _stream(stream)))
+    return y
+
+
+def fp8_gemm_grouped_scaled(qa, s_tok, row_token, expert_offsets, qw, s_ch, y=None, ws=None, stream=None):
+    """Grouped MoE GEMM over expert-sorted routed rows -> y bf16 [R, N]."""
+    torch = _torch()
+    T, K, _ = _rows(qa, torch.uint8, "qa")
+    if not qa.is_contiguous():
+        raise ValueError("qa: expected contiguous [T, K]")
+    if qw.dtype != torch.uint8 or qw.dim() != 3 or not qw.is_contiguous() or not qw.is_cuda:
+        raise ValueError("qw: expected a contiguous uint8 CUDA tensor [E, N, K]")
+    E, N, K2 = qw.shape
+    if K2 != K:
+        raise ValueError("qa and qw disagree on K")
+    R = row_token.numel()
+    _vec(s_tok, torch.float32, "s_tok", T)
+    _vec(row_token, torch.int32, "row_token", R)
+    _vec(expert_offsets, torch.int32, "expert_offsets", E + 1)
+    if s_ch.dtype != torch.float32 or tuple(s_ch.shape) != (E, N) or not s_ch.is_contiguous():
+        raise ValueError("s_ch: expected a contiguous float32 [E, N] tensor")
+    if y is None:
+        y = torch.empty((R, N), dtype=torch.bfloat16, device=qa.device)
+    if y.dtype != torch.bfloat16 or tuple(y.shape) != (R, N) or not y.is_contiguous():
+        raise ValueError("y: expected a contiguous bf16 [R, N] tensor")
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check("fp8_gemm_grouped_scaled",
+           lib().fp8_gemm_grouped_scaled(_ptr(qa), _ptr(s_tok), _ptr(row_token), _ptr(expert_offsets), _ptr(qw),
+                                         _ptr(s_ch), _ptr(y), T, R, E, N, K, _ptr(ws), ws_bytes, _stream(stream)))
+    return y

@@ -1,0 +1,192 @@
+// C ABI of the unified-FP8 linear layer: host-side validation and dispatch.
+//
+// Every entry point checks its arguments on the host first and returns a
+// status without touching the device when they are invalid; only then does it
+// enqueue kernels on the caller's stream.  No memory is allocated and no state
+// is kept between calls.
+#include "../../include/fp8w8a8.h"
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstdint>
+
+#include "kernels.hpp"
+
+namespace {
+
+constexpr int64_t kMaxDim = INT32_MAX;  // kernels index rows and columns with 32-bit ints
+constexpr size_t kAlign = 256;          // workspace sub-buffer alignment
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// a * b without int64 overflow (a, b >= 0)
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+    if (a != 0 && b > INT64_MAX / a) return false;
+    *out = a * b;
+    return true;
+}
+
+fp8_status_t check_dims(int64_t M, int64_t N, int64_t K) {
+    if (M < 0 || N < 0 || K < 0) return FP8_ERR_INVALID_ARGUMENT;
+    if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return FP8_ERR_UNSUPPORTED;
+    if (K % 16 != 0) return FP8_ERR_UNSUPPORTED;
+    return FP8_OK;
+}
+
+// A row-major matrix argument: rows x cols elements of `elem` bytes, stride
+// ld.  Input operands are read in 16-byte pieces, so their row stride must be
+// a multiple of 16 bytes (strided_ok = false); the BF16 output may have any
+// row stride (strided_ok = true).
+fp8_status_t check_matrix(const void* p, int64_t rows, int64_t cols, int64_t ld, int64_t elem,
+                          bool strided_ok = false) {
+    if (rows > 0 && cols > 0 && p == nullptr) return FP8_ERR_INVALID_ARGUMENT;
+    if (rows > 0 && ld < cols) return FP8_ERR_INVALID_ARGUMENT;
+    int64_t span, bytes;
+    if (!mul_ok(rows, ld, &span) || !mul_ok(span, elem, &bytes)) return FP8_ERR_INVALID_ARGUMENT;
+    if (rows > 0 && cols > 0) {
+        if (!aligned16(p)) return FP8_ERR_UNSUPPORTED;
+        if (!strided_ok && (ld * elem) % 16 != 0) return FP8_ERR_UNSUPPORTED;
+    }
+    return FP8_OK;
+}
+
+fp8_status_t check_vector(const void* p, int64_t n) {
+    if (n > 0 && p == nullptr) return FP8_ERR_INVALID_ARGUMENT;
+    if (n > 0 && !aligned16(p)) return FP8_ERR_UNSUPPORTED;
+    return FP8_OK;
+}
+
+#define FP8_TRY(expr)                          \
+    do {                                       \
+        fp8_status_t s_ = (expr);              \
+        if (s_ != FP8_OK) return s_;           \
+    } while (0)
+
+fp8_status_t from_hip(hipError_t e) { return e == hipSuccess ? FP8_OK : FP8_ERR_DEVICE; }
+
+// Bytes the GEMM path itself needs for an M x N x K problem (none today).
+size_t gemm_ws_bytes(int64_t, int64_t, int64_t) { return 0; }
+
+// Bytes the fused path stages its activation codes and scales in.
+size_t fused_stage_bytes(int64_t M, int64_t K) {
+    return round_up((size_t)M * (size_t)K, kAlign) + round_up((size_t)M * sizeof(float), kAlign);
+}
+
+fp8_status_t gemm_dispatch(const uint8_t* qa, int64_t lda, const float* s_tok, const uint8_t* qw, int64_t ldw,
+                           const float* s_ch, uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                           hipStream_t stream) {
+    if (M <= fp8k::kSkinnyMaxM)
+        return from_hip(fp8k::launch_gemm_skinny(qa, lda, s_tok, qw, ldw, s_ch, y, ldy, M, N, K, stream));
+    return from_hip(fp8k::launch_gemm_tiled(qa, lda, s_tok, qw, ldw, s_ch, y, ldy, M, N, K, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fp8_status_string(fp8_status_t status) {
+    switch (status) {
+        case FP8_OK: return "FP8_OK";
+        case FP8_ERR_INVALID_ARGUMENT: return "FP8_ERR_INVALID_ARGUMENT";
+        case FP8_ERR_UNSUPPORTED: return "FP8_ERR_UNSUPPORTED";
+        case FP8_ERR_WORKSPACE: return "FP8_ERR_WORKSPACE";
+        case FP8_ERR_DEVICE: return "FP8_ERR_DEVICE";
+    }
+    return "FP8_ERR_UNKNOWN";
+}
+
+size_t fp8_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (check_dims(M, N, K) == FP8_ERR_INVALID_ARGUMENT) return SIZE_MAX;
+    int64_t mk;
+    if (!mul_ok(M, K, &mk)) return SIZE_MAX;
+    return fused_stage_bytes(M, K) + gemm_ws_bytes(M, N, K);
+}
+
+size_t fp8_grouped_workspace_bytes(int64_t T, int64_t R, int64_t E, int64_t N, int64_t K) {
+    if (T < 0 || R < 0 || E < 0 || N < 0 || K < 0) return SIZE_MAX;
+    return 0;
+}
+
+fp8_status_t fp8_quantize_per_token(const float* x, int64_t rows, int64_t K, int64_t ldx, uint8_t* q,
+                                    int64_t ldq, float* scales, hipStream_t stream) {
+    FP8_TRY(check_dims(rows, 1, K));
+    FP8_TRY(check_matrix(x, rows, K, ldx, 4));
+    FP8_TRY(check_matrix(q, rows, K, ldq, 1));
+    FP8_TRY(check_vector(scales, rows));
+    if (rows == 0) return FP8_OK;
+    return from_hip(fp8k::launch_quantize_rows(x, ldx, q, ldq, scales, rows, K, stream));
+}
+
+fp8_status_t fp8_gemm_scaled(const uint8_t* qa, int64_t lda, const float* s_tok, const uint8_t* qw,
+                             int64_t ldw, const float* s_ch, uint16_t* y, int64_t ldy, int64_t M, int64_t N,
+                             int64_t K, void* ws, size_t ws_bytes, hipStream_t stream) {
+    FP8_TRY(check_dims(M, N, K));
+    FP8_TRY(check_matrix(qa, M, K, lda, 1));
+    FP8_TRY(check_matrix(qw, N, K, ldw, 1));
+    FP8_TRY(check_vector(s_tok, M));
+    FP8_TRY(check_vector(s_ch, N));
+    FP8_TRY(check_matrix(y, M, N, ldy, 2, true));
+    // operands are read only when the output is non-empty
+    if (M > 0 && N > 0 && K > 0 && (qa == nullptr || qw == nullptr)) return FP8_ERR_INVALID_ARGUMENT;
+    const size_t need = gemm_ws_bytes(M, N, K);
+    if (ws_bytes < need) return FP8_ERR_WORKSPACE;
+    if (need > 0 && ws == nullptr) return FP8_ERR_INVALID_ARGUMENT;
+    if (M == 0 || N == 0) return FP8_OK;
+    return gemm_dispatch(qa, lda, s_tok, qw, ldw, s_ch, y, ldy, M, N, K, stream);
+}
+
+fp8_status_t fp8_quant_gemm_fused(const float* x, int64_t ldx, const uint8_t* qw, int64_t ldw,
+                                  const float* s_ch, uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                                  uint8_t* qa_out, float* s_tok_out, void* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
+    FP8_TRY(check_dims(M, N, K));
+    FP8_TRY(check_matrix(x, M, K, ldx, 4));
+    FP8_TRY(check_matrix(qw, N, K, ldw, 1));
+    FP8_TRY(check_vector(s_ch, N));
+    FP8_TRY(check_matrix(y, M, N, ldy, 2, true));
+    if (qa_out) FP8_TRY(check_matrix(qa_out, M, K, K, 1));
+    if (s_tok_out) FP8_TRY(check_vector(s_tok_out, M));
+    if (M > 0 && N > 0 && K > 0 && qw == nullptr) return FP8_ERR_INVALID_ARGUMENT;
+    const size_t need = fp8_workspace_bytes(M, N, K);
+    if (ws_bytes < need) return FP8_ERR_WORKSPACE;
+    if (need > 0 && ws == nullptr) return FP8_ERR_INVALID_ARGUMENT;
+    if (need > 0 && !aligned16(ws)) return FP8_ERR_UNSUPPORTED;
+    if (M == 0) return FP8_OK;
+    uint8_t* base = static_cast<uint8_t*>(ws);
+    uint8_t* qa = qa_out ? qa_out : base;
+    float* s_tok = s_tok_out ? s_tok_out : reinterpret_cast<float*>(base + round_up((size_t)M * (size_t)K, kAlign));
+    FP8_TRY(from_hip(fp8k::launch_quantize_rows(x, ldx, qa, K, s_tok, M, K, stream)));
+    if (N == 0) return FP8_OK;
+    return gemm_dispatch(qa, K, s_tok, qw, ldw, s_ch, y, ldy, M, N, K, stream);
+}
+
+fp8_status_t fp8_gemm_grouped_scaled(const uint8_t* qa, const float* s_tok, const int32_t* row_token,
+                                     const int32_t* expert_offsets, const uint8_t* qw, const float* s_ch,
+                                     uint16_t* y, int64_t T, int64_t R, int64_t E, int64_t N, int64_t K,
+                                     void* ws, size_t ws_bytes, hipStream_t stream) {
+    (void)ws;
+    FP8_TRY(check_dims(T, N, K));
+    if (R < 0 || E < 0) return FP8_ERR_INVALID_ARGUMENT;
+    if (R > kMaxDim || E > 1024) return FP8_ERR_UNSUPPORTED;
+    if (R > 0 && E == 0) return FP8_ERR_INVALID_ARGUMENT;
+    if (R > 0 && T == 0) return FP8_ERR_INVALID_ARGUMENT;
+    FP8_TRY(check_matrix(qa, T, K, K, 1));
+    FP8_TRY(check_vector(s_tok, T));
+    FP8_TRY(check_vector(row_token, R));
+    FP8_TRY(check_vector(expert_offsets, R > 0 ? E + 1 : 0));
+    int64_t en;
+    if (!mul_ok(E, N, &en)) return FP8_ERR_INVALID_ARGUMENT;
+    FP8_TRY(check_matrix(qw, en, K, K, 1));
+    FP8_TRY(check_vector(s_ch, en));
+    FP8_TRY(check_matrix(y, R, N, N, 2, true));
+    if (R > 0 && N > 0 && K > 0 && (qa == nullptr || qw == nullptr)) return FP8_ERR_INVALID_ARGUMENT;
+    if (ws_bytes < fp8_grouped_workspace_bytes(T, R, E, N, K)) return FP8_ERR_WORKSPACE;
+    if (R == 0 || N == 0) return FP8_OK;
+    return from_hip(fp8k::launch_gemm_grouped(qa, s_tok, row_token, expert_offsets, qw, s_ch, y, T, R, E, N, K,
+                                              stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,33 @@
+// Launchers of the gfx950 kernels (internal to the library; the C ABI in
+// include/fp8w8a8.h validates arguments before calling these).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fp8k {
+
+// Per-row absmax quantization (quantize.hip).
+hipError_t launch_quantize_rows(const float* x, int64_t ldx, uint8_t* q, int64_t ldq, float* scales,
+                                int64_t rows, int64_t K, hipStream_t stream);
+
+// Largest M the skinny (decode) kernel takes.
+constexpr int64_t kSkinnyMaxM = 64;
+
+// Skinny-M scaled GEMM, M <= kSkinnyMaxM (gemm_skinny.hip).
+hipError_t launch_gemm_skinny(const uint8_t* qa, int64_t lda, const float* s_tok, const uint8_t* qw,
+                              int64_t ldw, const float* s_ch, uint16_t* y, int64_t ldy, int64_t M, int64_t N,
+                              int64_t K, hipStream_t stream);
+
+// LDS-tiled MFMA scaled GEMM for larger M (gemm_tiled.hip).
+hipError_t launch_gemm_tiled(const uint8_t* qa, int64_t lda, const float* s_tok, const uint8_t* qw,
+                             int64_t ldw, const float* s_ch, uint16_t* y, int64_t ldy, int64_t M, int64_t N,
+                             int64_t K, hipStream_t stream);
+
+// Grouped (MoE) scaled GEMM (gemm_tiled.hip).
+hipError_t launch_gemm_grouped(const uint8_t* qa, const float* s_tok, const int32_t* row_token,
+                               const int32_t* offsets, const uint8_t* qw, const float* s_ch, uint16_t* y,
+                               int64_t T, int64_t R, int64_t E, int64_t N, int64_t K, hipStream_t stream);
+
+}  // namespace fp8k

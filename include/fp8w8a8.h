@@ -1,0 +1,143 @@
+/*
+ * fp8w8a8.h -- C ABI of the MI355X (gfx950) unified-FP8 linear layer.
+ *
+ * The operation (from the FP8 inference pages this library implements):
+ *   - activations are quantized per token to OCP FP8 E4M3 with a dynamic
+ *     scale s_tok = max(fl32(rowmax|x| / 448), 1e-12f), codes enc(fl32(x/s))
+ *     rounded to nearest even and saturating at +-448
+ *     (Llama 3 FP8 page, §1.1 range and §3.1 absmax/448 conversion;
+ *      DeepSeek V4 950 page, §2.4 per-token activation scales computed on the
+ *      fly, §3.1 step 3; FP8 deployment page, §2.3 clamp to +-448);
+ *   - weights arrive pre-quantized to E4M3 with one scale per output channel
+ *     (same conversion, applied offline to each row of W[N,K]);
+ *   - the GEMM multiplies E4M3 by E4M3 with FP32 accumulation
+ *     (DeepSeek V4 950 page, §2.3) and a dequantizing epilogue writes
+ *     y[m,n] = bf16_rne(acc[m,n] * (s_tok[m] * s_ch[n])).
+ *
+ * Layouts (row-major, unit stride along the last dimension):
+ *   x      fp32  [M, K]  row stride ldx >= K      activations
+ *   qa     u8    [M, K]  row stride lda >= K      activation codes
+ *   qw     u8    [N, K]  row stride ldw >= K      weight codes (nn.Linear [out, in])
+ *   s_tok  fp32  [M]     per-token scales
+ *   s_ch   fp32  [N]     per-output-channel scales
+ *   y      bf16  [M, N]  row stride ldy >= N      stored as uint16 bit patterns
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers are device pointers the caller owns; buffers must stay alive
+ *     until the work enqueued on `stream` completes.  The library allocates
+ *     no memory and keeps no state between calls: it is re-entrant.
+ *   - Every call is asynchronous on `stream` (0 = the default stream).
+ *   - Arguments are validated on the host before anything is enqueued; on an
+ *     error nothing is enqueued and no buffer is touched.
+ *       FP8_ERR_INVALID_ARGUMENT  null pointer with a non-empty extent,
+ *                                 negative extent, leading dimension below the
+ *                                 row length, or a size that overflows int64;
+ *       FP8_ERR_UNSUPPORTED       K not a multiple of 16, an extent above
+ *                                 2^31 - 1, a pointer not 16-byte aligned, or
+ *                                 an input row stride (x, qa, qw) that is not
+ *                                 a multiple of 16 bytes (y may have any
+ *                                 row stride ldy >= N);
+ *       FP8_ERR_WORKSPACE         ws_bytes below the documented requirement;
+ *       FP8_ERR_DEVICE            the HIP runtime reported a launch error.
+ *   - An empty problem (M == 0, R == 0 or N == 0) is a no-op returning FP8_OK.
+ *     K == 0 is valid for the GEMMs (y = 0) and for the quantizer (scales are
+ *     the 1e-12 floor).
+ *   - Inputs are assumed finite.  Calls that share a workspace must not run
+ *     concurrently.
+ */
+#ifndef FP8W8A8_H
+#define FP8W8A8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FP8_OK = 0,
+    FP8_ERR_INVALID_ARGUMENT = 1,
+    FP8_ERR_UNSUPPORTED = 2,
+    FP8_ERR_WORKSPACE = 3,
+    FP8_ERR_DEVICE = 4
+} fp8_status_t;
+
+/*
+ * Per-row absmax quantization to E4M3 (Llama 3 FP8 page, §3.1; applied per
+ * token to activations, DeepSeek V4 950 page §2.4, and per output channel to
+ * weights, the offline conversion of the same page's §3.1).
+ *   scales[r] = max(fl32(max_k |x[r,k]|) / 448), 1e-12f)
+ *   q[r,k]    = E4M3 code of fl32(x[r,k] / scales[r]), RNE, saturating +-448
+ * x: fp32 [rows, K], stride ldx; q: u8 [rows, K], stride ldq; scales: [rows].
+ * No workspace.
+ */
+fp8_status_t fp8_quantize_per_token(const float* x, int64_t rows, int64_t K, int64_t ldx,
+                                    uint8_t* q, int64_t ldq, float* scales,
+                                    hipStream_t stream);
+
+/*
+ * Scaled FP8 GEMM with BF16 output (DeepSeek V4 950 page, §2.3 FP8 inputs
+ * with FP32 accumulation; §2.4 per-token x per-channel scales):
+ *   y[m,n] = bf16_rne( (sum_k e4m3(qa[m,k]) * e4m3(qw[n,k])) * (s_tok[m] * s_ch[n]) )
+ * Skinny M (decode, M <= 64) streams W once from HBM; larger M runs the
+ * LDS-tiled MFMA kernel.  ws: device scratch of at least
+ * fp8_workspace_bytes(M, N, K) bytes (may be NULL when that is 0).
+ */
+fp8_status_t fp8_gemm_scaled(const uint8_t* qa, int64_t lda, const float* s_tok,
+                             const uint8_t* qw, int64_t ldw, const float* s_ch,
+                             uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                             void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Quantize-then-GEMM in one call: the unified FP8 dataflow with no separate
+ * cast step exposed to the caller (DeepSeek V4 950 page, §1.3 and §2.3).
+ * Equivalent to fp8_quantize_per_token(x) followed by fp8_gemm_scaled.
+ * qa_out [M, K] (stride K) and s_tok_out [M] are optional (NULL allowed);
+ * when given they receive the activation codes and scales.  ws must hold at
+ * least fp8_workspace_bytes(M, N, K) bytes.
+ */
+fp8_status_t fp8_quant_gemm_fused(const float* x, int64_t ldx, const uint8_t* qw, int64_t ldw,
+                                  const float* s_ch, uint16_t* y, int64_t ldy,
+                                  int64_t M, int64_t N, int64_t K,
+                                  uint8_t* qa_out, float* s_tok_out,
+                                  void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Grouped (MoE expert) scaled FP8 GEMM (DeepSeek V4 950 page, §2.3 item 5:
+ * expert computation entirely in FP8; §2.4 per-channel scales per expert).
+ * Routed rows are sorted by expert: rows [expert_offsets[e], expert_offsets[e+1])
+ * belong to expert e, and routed row r reads token row_token[r]:
+ *   y[r,n] = bf16_rne( (sum_k e4m3(qa[t,k]) * e4m3(qw[e,n,k])) * (s_tok[t] * s_ch[e,n]) ),
+ *   t = row_token[r]
+ * qa: u8 [T, K] (stride K); s_tok: [T]; row_token: int32 [R] (device);
+ * expert_offsets: int32 [E+1] (device), non-decreasing, offsets[0] = 0,
+ * offsets[E] = R; qw: u8 [E, N, K]; s_ch: fp32 [E, N]; y: bf16 [R, N] (stride N).
+ * The routing arrays are read on the device and not validated there: offsets
+ * that are not non-decreasing in [0, R], or tokens outside [0, T), are
+ * undefined behaviour.  E <= 1024.  ws must hold at least
+ * fp8_grouped_workspace_bytes(...) bytes (currently 0: ws may be NULL).
+ */
+fp8_status_t fp8_gemm_grouped_scaled(const uint8_t* qa, const float* s_tok,
+                                     const int32_t* row_token, const int32_t* expert_offsets,
+                                     const uint8_t* qw, const float* s_ch, uint16_t* y,
+                                     int64_t T, int64_t R, int64_t E, int64_t N, int64_t K,
+                                     void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes fp8_gemm_scaled and fp8_quant_gemm_fused need for this
+ * shape (host-only, pure; 0 when none is needed; SIZE_MAX for invalid sizes). */
+size_t fp8_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/* Workspace bytes fp8_gemm_grouped_scaled needs (host-only, pure). */
+size_t fp8_grouped_workspace_bytes(int64_t T, int64_t R, int64_t E, int64_t N, int64_t K);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* fp8_status_string(fp8_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8W8A8_H */

@@ -39,6 +39,8 @@ def lib():
         L.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
         L.oracle_e4m3_encode.restype = ctypes.c_uint8
         L.oracle_e4m3_encode.argtypes = [ctypes.c_float]
+        L.oracle_e4m3_encode_array.restype = None
+        L.oracle_e4m3_encode_array.argtypes = [vp, i64, vp]
         L.oracle_quantize_rows.restype = None
         L.oracle_quantize_rows.argtypes = [vp, i64, i64, i64, vp, i64, vp]
         L.oracle_gemm_ref.restype = None
@@ -79,10 +81,10 @@ def decode(codes):
 
 def encode(values):
     """float32 array -> E4M3 codes (RNE, saturating)."""
-    v = _c(values, np.float32).ravel()
-    L = lib()
-    return np.fromiter((L.oracle_e4m3_encode(float(x)) for x in v), dtype=np.uint8, count=v.size).reshape(
-        np.shape(values))
+    v = _c(values, np.float32)
+    out = np.empty(v.shape, dtype=np.uint8)
+    lib().oracle_e4m3_encode_array(_p(v), v.size, _p(out))
+    return out
 
 
 def encode_fn_address():

@@ -91,6 +91,12 @@ uint8_t oracle_e4m3_encode(float v) {
     return (uint8_t)(sign | (E << 3) | m);
 }
 
+/* Element-wise encode of an array (the codec above, applied n times). */
+void oracle_e4m3_encode_array(const float* v, int64_t n, uint8_t* out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_e4m3_encode(v[i]);
+}
+
 /* ------------------------------------------------------------ quantizer -- */
 
 /* Per-row absmax quantization, the [L3] §3.1 conversion applied to any

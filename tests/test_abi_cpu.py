@@ -1,0 +1,176 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol the header
+declares, and rejects bad arguments on the host before any launch (CPU only:
+only error paths and empty problems are called, none of which reach the HIP
+runtime)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import fp8_w8a8_quantized_quantize_amd as fp8
+from fp8_w8a8_quantized_quantize_amd import (FP8_ERR_INVALID_ARGUMENT, FP8_ERR_UNSUPPORTED, FP8_ERR_WORKSPACE,
+                                             FP8_OK)
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8w8a8.h")
+
+P = 0x10000     # a 16-byte-aligned fake device address: never dereferenced on these paths
+Q = 0x20000
+MIS = 0x10008   # 8-byte aligned only
+S0 = ctypes.c_void_p(0)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(fp8_[a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    L = fp8.lib()
+    names = declared_functions()
+    assert set(names) == set(fp8.EXPORTS), names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    for code, name in [(0, "FP8_OK"), (1, "FP8_ERR_INVALID_ARGUMENT"), (2, "FP8_ERR_UNSUPPORTED"),
+                       (3, "FP8_ERR_WORKSPACE"), (4, "FP8_ERR_DEVICE")]:
+        assert fp8.fp8_status_string(code) == name
+    assert fp8.fp8_status_string(99) == "FP8_ERR_UNKNOWN"
+
+
+def test_workspace_bytes():
+    # fused path stages M*K codes and M scales, each rounded up to 256 bytes
+    assert fp8.fp8_workspace_bytes(8, 14336, 4096) == 8 * 4096 + 256
+    assert fp8.fp8_workspace_bytes(8192, 8192, 8192) == 8192 * 8192 + 8192 * 4
+    assert fp8.fp8_workspace_bytes(0, 5, 16) == 0
+    assert fp8.fp8_workspace_bytes(-1, 5, 16) == ctypes.c_size_t(-1).value
+    assert fp8.fp8_grouped_workspace_bytes(4096, 32768, 64, 2048, 7168) == 0
+
+
+def q(*a):
+    return fp8.lib().fp8_quantize_per_token(*a)
+
+
+def test_quantize_validation():
+    # x, rows, K, ldx, q, ldq, scales, stream
+    assert q(P, 4, 15, 16, Q, 16, P, S0) == FP8_ERR_UNSUPPORTED          # K % 16
+    assert q(P, 4, 16, 8, Q, 16, P, S0) == FP8_ERR_INVALID_ARGUMENT      # ldx < K
+    assert q(P, 4, 16, 16, Q, 8, P, S0) == FP8_ERR_INVALID_ARGUMENT      # ldq < K
+    assert q(0, 4, 16, 16, Q, 16, P, S0) == FP8_ERR_INVALID_ARGUMENT     # null x
+    assert q(P, 4, 16, 16, 0, 16, P, S0) == FP8_ERR_INVALID_ARGUMENT     # null q
+    assert q(P, 4, 16, 16, Q, 16, 0, S0) == FP8_ERR_INVALID_ARGUMENT     # null scales
+    assert q(P, -1, 16, 16, Q, 16, P, S0) == FP8_ERR_INVALID_ARGUMENT    # negative rows
+    assert q(MIS, 4, 16, 16, Q, 16, P, S0) == FP8_ERR_UNSUPPORTED        # misaligned x
+    assert q(P, 4, 16, 18, Q, 16, P, S0) == FP8_ERR_UNSUPPORTED          # x stride not 16 B
+    assert q(P, 4, 16, 16, Q, 24, P, S0) == FP8_ERR_UNSUPPORTED          # q stride not 16 B
+    assert q(P, 1 << 62, 16, 16, Q, 16, P, S0) == FP8_ERR_UNSUPPORTED    # beyond 32-bit rows
+    assert q(P, 1 << 30, 1 << 30, 1 << 40, Q, 1 << 30, P, S0) == FP8_ERR_INVALID_ARGUMENT  # overflow
+    assert q(0, 0, 16, 16, 0, 16, 0, S0) == FP8_OK                      # empty: no-op
+
+
+def g(*a):
+    return fp8.lib().fp8_gemm_scaled(*a)
+
+
+def test_gemm_validation():
+    # qa, lda, s_tok, qw, ldw, s_ch, y, ldy, M, N, K, ws, ws_bytes, stream
+    ok = [P, 64, P, Q, 64, P, Q, 32, 4, 32, 64, 0, 0, S0]
+
+    def with_(**kw):
+        a = list(ok)
+        idx = dict(qa=0, lda=1, s_tok=2, qw=3, ldw=4, s_ch=5, y=6, ldy=7, M=8, N=9, K=10, ws=11, wsb=12)
+        for k, v in kw.items():
+            a[idx[k]] = v
+        return g(*a)
+
+    assert with_(K=40, lda=48, ldw=48) == FP8_ERR_UNSUPPORTED
+    assert with_(lda=32) == FP8_ERR_INVALID_ARGUMENT
+    assert with_(ldw=48) == FP8_ERR_INVALID_ARGUMENT
+    assert with_(ldy=16) == FP8_ERR_INVALID_ARGUMENT
+    assert with_(ldw=72) == FP8_ERR_UNSUPPORTED          # weight stride not 16 B
+    assert with_(lda=72) == FP8_ERR_UNSUPPORTED          # activation-code stride not 16 B
+    assert with_(y=MIS) == FP8_ERR_UNSUPPORTED
+    assert with_(qa=0) == FP8_ERR_INVALID_ARGUMENT
+    assert with_(qw=0) == FP8_ERR_INVALID_ARGUMENT
+    assert with_(s_tok=0) == FP8_ERR_INVALID_ARGUMENT
+    assert with_(s_ch=0) == FP8_ERR_INVALID_ARGUMENT
+    assert with_(y=0) == FP8_ERR_INVALID_ARGUMENT
+    assert with_(s_ch=MIS) == FP8_ERR_UNSUPPORTED
+    assert with_(M=-3) == FP8_ERR_INVALID_ARGUMENT
+    assert with_(M=0, qa=0, s_tok=0, y=0) == FP8_OK       # empty: no-op
+    assert with_(N=0, qw=0, s_ch=0, y=0) == FP8_OK
+
+
+def f(*a):
+    return fp8.lib().fp8_quant_gemm_fused(*a)
+
+
+def test_fused_validation():
+    # x, ldx, qw, ldw, s_ch, y, ldy, M, N, K, qa_out, s_tok_out, ws, ws_bytes, stream
+    need = fp8.fp8_workspace_bytes(4, 32, 64)
+    base = [P, 64, Q, 64, P, Q, 32, 4, 32, 64, 0, 0, P, need, S0]
+
+    def with_(**kw):
+        a = list(base)
+        idx = dict(x=0, ldx=1, qw=2, ldw=3, s_ch=4, y=5, ldy=6, M=7, N=8, K=9, qa=10, st=11, ws=12, wsb=13)
+        for k, v in kw.items():
+            a[idx[k]] = v
+        return f(*a)
+
+    assert with_(wsb=need - 1) == FP8_ERR_WORKSPACE
+    assert with_(ws=0) == FP8_ERR_INVALID_ARGUMENT
+    assert with_(ws=MIS) == FP8_ERR_UNSUPPORTED
+    assert with_(x=0) == FP8_ERR_INVALID_ARGUMENT
+    assert with_(ldx=60) == FP8_ERR_INVALID_ARGUMENT
+    assert with_(K=24, ldx=32, ldw=32) == FP8_ERR_UNSUPPORTED
+    assert with_(qa=MIS) == FP8_ERR_UNSUPPORTED
+    assert with_(st=MIS) == FP8_ERR_UNSUPPORTED
+    assert with_(M=0, x=0, y=0, ws=0, wsb=0) == FP8_OK
+
+
+def gg(*a):
+    return fp8.lib().fp8_gemm_grouped_scaled(*a)
+
+
+def test_grouped_validation():
+    # qa, s_tok, row_token, offsets, qw, s_ch, y, T, R, E, N, K, ws, ws_bytes, stream
+    base = [P, P, P, P, Q, P, Q, 8, 16, 4, 32, 64, 0, 0, S0]
+
+    def with_(**kw):
+        a = list(base)
+        idx = dict(qa=0, st=1, rt=2, off=3, qw=4, sc=5, y=6, T=7, R=8, E=9, N=10, K=11)
+        for k, v in kw.items():
+            a[idx[k]] = v
+        return gg(*a)
+
+    assert with_(K=8) == FP8_ERR_UNSUPPORTED
+    assert with_(E=2000) == FP8_ERR_UNSUPPORTED
+    assert with_(E=0) == FP8_ERR_INVALID_ARGUMENT
+    assert with_(T=0, qa=0, st=0) == FP8_ERR_INVALID_ARGUMENT
+    assert with_(rt=0) == FP8_ERR_INVALID_ARGUMENT
+    assert with_(off=0) == FP8_ERR_INVALID_ARGUMENT
+    assert with_(qw=0) == FP8_ERR_INVALID_ARGUMENT
+    assert with_(sc=MIS) == FP8_ERR_UNSUPPORTED
+    assert with_(R=-1) == FP8_ERR_INVALID_ARGUMENT
+    assert with_(R=0, rt=0, off=0, y=0) == FP8_OK
+
+
+@pytest.mark.parametrize("name", ["fp8_quantize_per_token", "fp8_gemm_scaled", "fp8_quant_gemm_fused",
+                                  "fp8_gemm_grouped_scaled"])
+def test_python_binding_requires_cuda_tensors(name):
+    import torch
+    fn = getattr(fp8, name)
+    with pytest.raises((TypeError, ValueError)):
+        if name == "fp8_quantize_per_token":
+            fn(torch.zeros(2, 16))
+        elif name == "fp8_gemm_scaled":
+            fn(torch.zeros(2, 16, dtype=torch.uint8), torch.ones(2), torch.zeros(2, 16, dtype=torch.uint8), torch.ones(2))
+        elif name == "fp8_quant_gemm_fused":
+            fn(torch.zeros(2, 16), torch.zeros(2, 16, dtype=torch.uint8), torch.ones(2))
+        else:
+            fn(torch.zeros(2, 16, dtype=torch.uint8), torch.ones(2), torch.zeros(2, dtype=torch.int32),
+               torch.zeros(2, dtype=torch.int32), torch.zeros(1, 2, 16, dtype=torch.uint8), torch.ones(1, 2))
