@@ -1,0 +1,307 @@
+#!/usr/bin/env python3
+"""Benchmark of the unified-FP8 (W8A8) linear layer on one MI355X.
+
+One step = one pass of the hot path over one batch of synthetic input:
+  dense workloads: fp8_quant_gemm_fused (per-token E4M3 quantization of the
+                   activations + FP8 GEMM with the s_tok*s_ch BF16 epilogue)
+                   against pre-quantized weights;
+  MoE workload:    per-token quantization of the token activations +
+                   fp8_gemm_grouped_scaled over the expert-sorted routed rows.
+Weight quantization is the offline step and is not timed.
+
+Default workload: the Llama-3-8B FFN up-projection decode (M=8, K=4096,
+N=14336), reported as algorithmic HBM GB/s.  Decode workloads rotate several
+weight copies (>= 512 MB in total) so that the 256 MB Infinity Cache cannot
+serve the weights across steps.
+
+The JSON line adds
+  roofline:     the dominant kernel (the GEMM) timed alone with HIP events on
+                the launch stream, algorithmic bytes (or FLOPs) per launch over
+                its average duration, against the MI355X peak;
+  cpu_baseline: the CPU oracle timed on the host on a bounded sample of the
+                same workload.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "FP8 W8A8 GEMM TFLOPS (prefill) & HBM GB/s (decode M≤64), % of roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA
+ROTATE_BYTES = 512 << 20       # weight copies rotated per decode workload
+DEFAULT_WORKLOAD = "llama3-8b-decode-up"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+KERNEL_SOURCES = {
+    "skinny": ["gemm_skinny.hip", "device_common.hpp"],
+    "tiled": ["gemm_tiled.hip", "device_common.hpp"],
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU-oracle sample time")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile", action="store_true",
+                    help="few steps, no CPU baseline: for runs under rocprofv3")
+    return ap.parse_args()
+
+
+def kernel_source_hash(kind):
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, "fp8_w8a8_quantized_quantize_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload, kind):
+    """HBM bytes per launch from the committed rocprofv3 PMC summary, if it was
+    taken on the current kernel source; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    src = kernel_source_hash(kind)
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            m = re.match(r"^TRAFFIC\s+(\{.*\})\s*$", line.strip())
+            if not m:
+                continue
+            rec = json.loads(m.group(1))
+            if rec.get("workload") == workload and rec.get("source") == src:
+                return rec.get("hbm_bytes_per_launch")
+    return None
+
+
+def gen_dense(w, seed):
+    import synth
+    x, _ = synth.activations(w["M"], w["K"], synth.workload_outliers(w), w["mult"], seed=seed)
+    wt = synth.weights(w["N"], w["K"], seed=seed)
+    return x, wt
+
+
+def time_loop(fn, n, warmup):
+    """Run fn(i) warmup times, then n times between HIP events on the current
+    stream; returns (total ms, per-step ms list)."""
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    evs[0].record()
+    for i in range(n):
+        fn(i)
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(n)]
+    return evs[0].elapsed_time(evs[n]), per
+
+
+def pct(v, q):
+    v = sorted(v)
+    return v[min(len(v) - 1, max(0, int(round(q * (len(v) - 1)))))]
+
+
+def cpu_baseline_dense(w, x, wt_q, sc, target_s):
+    """The CPU oracle (per-token quantization + exact binary64 GEMM against all
+    weight rows) on the step's activation rows: every row, repeated for about
+    target_s seconds when a pass is short (decode); otherwise the first rows
+    that take about target_s seconds (prefill)."""
+    import oracle
+    M, N, K = w["M"], w["N"], w["K"]
+    rows = min(M, 8)
+    t0 = time.perf_counter()
+    qa, st = oracle.quantize_rows(x[:rows])
+    oracle.gemm_ref(qa, st, wt_q, sc)
+    dt = max(time.perf_counter() - t0, 1e-6)
+    if rows < M:
+        rows = int(min(M, max(rows, rows * target_s / dt)))
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        qa, st = oracle.quantize_rows(x[:rows])
+        oracle.gemm_ref(qa, st, wt_q, sc)
+        reps += 1
+        elapsed = time.perf_counter() - t0
+        if rows < M or elapsed >= target_s:
+            break
+    flops = 2.0 * reps * rows * N * K
+    bytes_ = reps * (rows * (4 * K + 2 * N) + N * K + 4 * N)
+    sample = (f"{reps} pass(es) over {rows} of {M} activation rows: per-token quantization + exact binary64 "
+              f"GEMM against all {N} weight rows")
+    return dict(elapsed=elapsed, flops=flops, bytes=bytes_, cores=oracle.num_threads(), sample=sample)
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the shard design is described in DESIGN.md); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import fp8_w8a8_quantized_quantize_amd as fp8
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X (no GPU visible)", file=sys.stderr)
+        sys.exit(3)
+    fp8.lib()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    w = synth.WORKLOADS[args.workload]
+    steps, warmup = args.steps, args.warmup
+    if args.profile:
+        steps, warmup = min(steps, 10), min(warmup, 3)
+    log = lambda *a: print(*a, file=sys.stderr, flush=True)
+
+    if w["kind"] == "dense":
+        M, N, K = w["M"], w["N"], w["K"]
+        log(f"[bench] {args.workload}: generating inputs M={M} N={N} K={K}")
+        x, wt = gen_dense(w, args.seed)
+        wq, sc = fp8.fp8_quantize_per_token(torch.from_numpy(wt).to(dev))  # offline weight conversion
+        wbytes = N * K
+        copies = max(1, math.ceil(ROTATE_BYTES / wbytes))
+        wcopies = [wq] + [wq.clone() for _ in range(copies - 1)]
+        xd = torch.from_numpy(x).to(dev)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(fp8.fp8_workspace_bytes(M, N, K), dtype=torch.uint8, device=dev)
+        qa = torch.empty((M, K), dtype=torch.uint8, device=dev)
+        st = torch.empty(M, dtype=torch.float32, device=dev)
+
+        def step(i):
+            fp8.fp8_quant_gemm_fused(xd, wcopies[i % copies], sc, y=y, ws=ws)
+
+        # the dominant kernel alone: the GEMM on pre-quantized activations
+        fp8.fp8_quantize_per_token(xd, q=qa, scales=st)
+
+        def gemm(i):
+            fp8.fp8_gemm_scaled(qa, st, wcopies[i % copies], sc, y=y)
+
+        log(f"[bench] {copies} weight copies; warmup {warmup}, timing {steps} steps")
+        total_ms, per = time_loop(step, steps, warmup)
+        gemm_ms, gemm_per = time_loop(gemm, steps, warmup)
+        ms = total_ms / steps
+        decode = M <= 64
+        flops = 2.0 * M * N * K
+        step_bytes = 4 * M * K + N * K + 4 * N + 2 * M * N           # fused: fp32 x in, codes W, s_ch, bf16 y out
+        gemm_bytes = M * K + 4 * M + N * K + 4 * N + 2 * M * N       # GEMM kernel: codes x, s_tok, W, s_ch, y
+        gemm_avg_ms = gemm_ms / steps
+        kind = "skinny" if decode else "tiled"
+        if decode:
+            value, unit = step_bytes / (ms * 1e-3) / 1e9, "GB/s"
+            achieved = gemm_bytes / (gemm_avg_ms * 1e-3) / 1e9
+            roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                        frac=round(achieved / HBM_PEAK_GBS, 4))
+        else:
+            value, unit = flops / (ms * 1e-3) / 1e12, "TFLOP/s"
+            achieved = flops / (gemm_avg_ms * 1e-3) / 1e12
+            roof = dict(bound="mfma", achieved=round(achieved, 1), peak=FP8_PEAK_TFLOPS, unit="TFLOP/s",
+                        frac=round(achieved / FP8_PEAK_TFLOPS, 4))
+        traffic = read_traffic(args.workload, kind)
+        roof["traffic"] = traffic
+        roof["kernel"] = f"gemm_{kind}_kernel"
+        roof["per_launch"] = (f"{gemm_bytes} algorithmic bytes" if decode else f"{flops:.6g} FLOP")
+        roof["avg_launch_us"] = round(gemm_avg_ms * 1e3, 3)
+        cfg = dict(workload=args.workload, M=M, N=N, K=K, seed=args.seed, weight_copies=copies,
+                   step="fp8_quant_gemm_fused", out="bf16")
+        extra = dict(step_us_median=round(pct(per, 0.5) * 1e3, 3), step_us_p10=round(pct(per, 0.1) * 1e3, 3),
+                     step_us_p90=round(pct(per, 0.9) * 1e3, 3), step_tflops=round(flops / (ms * 1e-3) / 1e12, 2),
+                     step_gbs=round(step_bytes / (ms * 1e-3) / 1e9, 1),
+                     gemm_us_median=round(pct(gemm_per, 0.5) * 1e3, 3))
+        cpu = None
+        if not args.no_cpu_baseline and not args.profile:
+            log("[bench] timing the CPU oracle")
+            wq_h = wq.cpu().numpy()
+            sc_h = sc.cpu().numpy()
+            r = cpu_baseline_dense(w, x, wq_h, sc_h, args.cpu_seconds)
+            cv = (r["bytes"] / r["elapsed"] / 1e9) if decode else (r["flops"] / r["elapsed"] / 1e12)
+            cpu = dict(value=round(cv, 6), unit=unit, cores=r["cores"], kind="oracle", sample=r["sample"],
+                       seconds=round(r["elapsed"], 2))
+    else:
+        T, E, k, N, K = w["T"], w["E"], w["topk"], w["N"], w["K"]
+        log(f"[bench] {args.workload}: generating inputs T={T} E={E} top-{k} N={N} K={K}")
+        te, rt, off = synth.routing(T, E, k, w["zipf"], seed=args.seed)
+        x, _ = synth.activations(T, K, synth.workload_outliers(w), w["mult"], seed=args.seed)
+        xd = torch.from_numpy(x).to(dev)
+        qw = torch.empty((E, N, K), dtype=torch.uint8, device=dev)
+        sc = torch.empty((E, N), dtype=torch.float32, device=dev)
+        for e0 in range(0, E, 8):
+            we = synth.expert_weights(E, N, K, seed=args.seed, experts=range(e0, e0 + 8)).reshape(8 * N, K)
+            fp8.fp8_quantize_per_token(torch.from_numpy(we).to(dev), q=qw[e0:e0 + 8].view(8 * N, K),
+                                       scales=sc[e0:e0 + 8].view(-1))
+        rtd, offd = torch.from_numpy(rt).to(dev), torch.from_numpy(off).to(dev)
+        R = rt.size
+        qa = torch.empty((T, K), dtype=torch.uint8, device=dev)
+        st = torch.empty(T, dtype=torch.float32, device=dev)
+        y = torch.empty((R, N), dtype=torch.bfloat16, device=dev)
+
+        def step(i):
+            fp8.fp8_quantize_per_token(xd, q=qa, scales=st)
+            fp8.fp8_gemm_grouped_scaled(qa, st, rtd, offd, qw, sc, y=y)
+
+        def gemm(i):
+            fp8.fp8_gemm_grouped_scaled(qa, st, rtd, offd, qw, sc, y=y)
+
+        total_ms, per = time_loop(step, steps, warmup)
+        gemm_ms, gemm_per = time_loop(gemm, steps, warmup)
+        ms = total_ms / steps
+        flops = 2.0 * R * N * K
+        gemm_bytes = E * N * K + 4 * E * N + T * K + 4 * T + 4 * R + 4 * (E + 1) + 2 * R * N
+        gemm_avg_ms = gemm_ms / steps
+        value, unit = flops / (ms * 1e-3) / 1e12, "TFLOP/s"
+        achieved = flops / (gemm_avg_ms * 1e-3) / 1e12
+        t_roof = max(flops / (FP8_PEAK_TFLOPS * 1e12), gemm_bytes / (HBM_PEAK_GBS * 1e9))
+        roof = dict(bound="mfma", achieved=round(achieved, 1), peak=FP8_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=round(achieved / FP8_PEAK_TFLOPS, 4), traffic=read_traffic(args.workload, "tiled"),
+                    kernel="gemm_tiled_kernel (grouped)", per_launch=f"{flops:.6g} FLOP",
+                    avg_launch_us=round(gemm_avg_ms * 1e3, 3),
+                    roofline_time_frac=round(t_roof / (gemm_avg_ms * 1e-3), 4),
+                    achieved_gbs=round(gemm_bytes / (gemm_avg_ms * 1e-3) / 1e9, 1))
+        cfg = dict(workload=args.workload, T=T, E=E, topk=k, N=N, K=K, R=R, zipf=w["zipf"], seed=args.seed,
+                   step="fp8_quantize_per_token + fp8_gemm_grouped_scaled", out="bf16")
+        extra = dict(step_us_median=round(pct(per, 0.5) * 1e3, 3), step_us_p10=round(pct(per, 0.1) * 1e3, 3),
+                     step_us_p90=round(pct(per, 0.9) * 1e3, 3), gemm_us_median=round(pct(gemm_per, 0.5) * 1e3, 3),
+                     expert_rows_max=int(np.diff(off).max()), expert_rows_min=int(np.diff(off).min()))
+        cpu = None
+        if not args.no_cpu_baseline and not args.profile:
+            import oracle
+            log("[bench] timing the CPU oracle")
+            qw_h, sc_h = qw.cpu().numpy(), sc.cpu().numpy()
+            rng = np.random.default_rng(0)
+            t0 = time.perf_counter()
+            qa_h, st_h = oracle.quantize_rows(x)
+            n_el, elapsed = 0, 0.0
+            while elapsed < args.cpu_seconds:
+                rs = rng.integers(0, R, 1 << 14)
+                ns = rng.integers(0, N, 1 << 14)
+                oracle.grouped_ref_sampled(qa_h, st_h, rt, off, qw_h, sc_h, rs, ns)
+                n_el += rs.size
+                elapsed = time.perf_counter() - t0
+            cpu = dict(value=round(2.0 * n_el * K / elapsed / 1e12, 6), unit="TFLOP/s", cores=oracle.num_threads(),
+                       kind="oracle", seconds=round(elapsed, 2),
+                       sample=f"quantize all {T} token rows + {n_el} random routed outputs (exact binary64 dots)")
+
+    out = {
+        "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8e4m3 (fp32 accumulate, bf16 out)", "data": "synthetic (seeded; no dataset, no trained weights)",
+        "config": cfg, "roofline": roof, "cpu_baseline": cpu, "detail": extra,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
