@@ -41,7 +41,7 @@ DEFAULT_WORKLOAD = "llama3-8b-decode-up"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 KERNEL_SOURCES = {
     "skinny": ["gemm_skinny.hip", "device_common.hpp"],
-    "tiled": ["gemm_tiled.hip", "device_common.hpp"],
+    "tiled": ["gemm_mfma.hip", "device_common.hpp"],
 }
 
 
