@@ -80,7 +80,7 @@ fp8_status_t gemm_dispatch(const uint8_t* qa, int64_t lda, const float* s_tok, c
                            hipStream_t stream) {
     if (M <= fp8k::kSkinnyMaxM)
         return from_hip(fp8k::launch_gemm_skinny(qa, lda, s_tok, qw, ldw, s_ch, y, ldy, M, N, K, stream));
-    if (K % 64 == 0)
+    if (K % 128 == 0)
         return from_hip(fp8k::launch_gemm_mfma(qa, lda, s_tok, qw, ldw, s_ch, y, ldy, M, N, K, stream));
     return from_hip(fp8k::launch_gemm_tiled(qa, lda, s_tok, qw, ldw, s_ch, y, ldy, M, N, K, stream));
 }
@@ -187,7 +187,7 @@ fp8_status_t fp8_gemm_grouped_scaled(const uint8_t* qa, const float* s_tok, cons
     if (R > 0 && N > 0 && K > 0 && (qa == nullptr || qw == nullptr)) return FP8_ERR_INVALID_ARGUMENT;
     if (ws_bytes < fp8_grouped_workspace_bytes(T, R, E, N, K)) return FP8_ERR_WORKSPACE;
     if (R == 0 || N == 0) return FP8_OK;
-    if (K % 64 == 0)
+    if (K % 128 == 0)
         return from_hip(fp8k::launch_gemm_grouped_mfma(qa, s_tok, row_token, expert_offsets, qw, s_ch, y, T, R, E,
                                                        N, K, stream));
     return from_hip(fp8k::launch_gemm_grouped(qa, s_tok, row_token, expert_offsets, qw, s_ch, y, T, R, E, N, K,

@@ -1,29 +1,38 @@
-// Multi-stage FP8 MFMA GEMM for gfx950 fed by direct global->LDS loads
+// Two-stage FP8 MFMA GEMM for gfx950 fed by direct global->LDS loads
 // (prefill-shaped M and the grouped MoE expert GEMM), FP32 accumulation and
 // the s_tok*s_ch dequantizing BF16 epilogue (DeepSeek V4 950 page, §2.3 and
 // §2.4; FP8 x FP8 with FP32 accumulation, precision/hardware page §2.3).
 //
 // Tile: BN weight rows (MFMA A operand) x BM activation rows (MFMA B operand),
-// 64 bytes of K per stage, STAGES stages in LDS.  Four waves in a 2 x 2 grid,
-// each owning (BN/2) x (BM/2) outputs as 32x32x64 FP8 MFMA tiles with 16
-// accumulators per lane.
+// 128 bytes of K per stage, two stages in LDS.  Four waves in a 2 x 2 grid,
+// each owning (BN/2) x (BM/2) outputs as 32x32x64 FP8 MFMA tiles (16
+// accumulators per lane); a stage is consumed as two 64-wide K halves.
 //
-// Data movement: global_load_lds_dwordx4 writes each wave's 1 KB of a stage
-// straight into LDS (no VGPR staging, no ds_write).  One DMA instruction
-// covers 16 rows x 64 bytes; lane l fetches row l/4, 16-byte piece
-// (l % 4) ^ swz(row), so the LDS image holds piece c of row r at position
-// c ^ swz(r).  swz(r) = ((r >> 1) ^ (r >> 2)) & 3 keeps the fragment reads
-// (32 rows x one 16-byte piece per wave read) free of bank conflicts for both
-// 8-lane/128-byte and 16-lane/256-byte LDS service groups.
+// Data movement: global_load_lds_dwordx4 writes a stage straight into LDS
+// (no VGPR staging, no ds_write).  One DMA instruction covers 8 rows x 128
+// bytes -- whole cache lines, which the L2->CU path delivers markedly faster
+// than half lines; lane l fetches row l / 8, 16-byte piece (l % 8) ^ swz(row),
+// so the LDS image holds piece c of row r at position c ^ swz(r).
+// swz(r) = (r ^ (r >> 3)) & 7 keeps the fragment reads (32 rows x one piece
+// per read) free of bank conflicts for 8-lane/128-byte and 16-lane/256-byte
+// LDS service groups alike.
 //
-// Pipeline per K step k (one barrier), STAGES-1 stages in flight:
-//   wait (vmcnt) for this wave's DMA of stage k; barrier (every wave's part of
-//   stage k has landed and every wave has finished reading stage k-1);
-//   issue the DMA of stage k+STAGES-1 into stage k-1's buffer;
-//   read the fragments of stage k and run its MFMAs.
-// The compiler does not track DMA-written LDS, so the waits are explicit
-// (s_waitcnt vmcnt with the number of younger DMA instructions) and compiler
-// memory fences keep LDS reads on their side of each wait and barrier.
+// Pipeline, step s (stage s in LDS, its first-half fragments in registers):
+//   first-half MFMAs of stage s, refilling each fragment register with the
+//   second half as soon as its last first-half MFMA has issued;
+//   wait (vmcnt) for this wave's DMA of stage s+1 and (lgkmcnt) for its reads
+//   of stage s; barrier: stage s+1 is complete in LDS and nobody reads stage
+//   s any more -> issue the DMA of stage s+2 into stage s's buffer;
+//   second-half MFMAs of stage s, refilling the registers with the first
+//   half of stage s+1.
+// One barrier per 32 MFMAs, LDS reads overlapped with MFMAs, a whole step of
+// MFMA time to hide each stage's load.  The compiler does not track
+// DMA-written LDS, so the waits are explicit and compiler memory fences keep
+// LDS reads on their side of each wait and barrier.
+//
+// The output tile leaves through LDS (scaled, BF16, swizzled) so that the
+// global stores are 16-byte row-contiguous; the tile's scales are staged in
+// LDS at the start.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -33,14 +42,14 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 
 namespace {
 
-constexpr int kDK = 64;       // K bytes per stage
+constexpr int kBK = 128;      // K bytes per stage
 constexpr int kThreadsM = 256;
 
 __device__ __forceinline__ v16f mfma_32x32x64_e4m3(const v8i& a, const v8i& b, const v16f& c) {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
-__device__ __forceinline__ int dswz(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
+__device__ __forceinline__ int dswz(int row) { return (row ^ (row >> 3)) & 7; }
 
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
@@ -73,12 +82,14 @@ __device__ __forceinline__ void block_barrier() {
     compiler_fence();
 }
 
-// One 32-row MFMA operand fragment from a stage tile of 64-byte rows:
-// lane l supplies row row0 + l % 32, pieces g and 2 + g (g = l / 32).
-__device__ __forceinline__ v8i read_frag(const uint8_t* tile, int row, int g) {
+// One 32-row MFMA operand fragment from a stage tile of 128-byte rows, K half
+// h: lane l supplies row row0 + l % 32, pieces 4h + g and 4h + 2 + g
+// (g = l / 32).  A and B fragments use the same piece order, so every k pairs
+// with itself in the dot product.
+__device__ __forceinline__ v8i read_frag(const uint8_t* tile, int row, int h, int g) {
     const int s = dswz(row);
-    const v4i lo = *reinterpret_cast<const v4i*>(tile + row * kDK + ((g ^ s) << 4));
-    const v4i hi = *reinterpret_cast<const v4i*>(tile + row * kDK + (((2 + g) ^ s) << 4));
+    const v4i lo = *reinterpret_cast<const v4i*>(tile + row * kBK + (((4 * h + g) ^ s) << 4));
+    const v4i hi = *reinterpret_cast<const v4i*>(tile + row * kBK + (((4 * h + 2 + g) ^ s) << 4));
     return join(lo, hi);
 }
 
@@ -146,12 +157,13 @@ template <int BN, int BM, int STAGES, int GROUP_M, bool GROUPED>
 __global__ __launch_bounds__(kThreadsM, 1) void gemm_mfma_kernel(MfmaArgs p) {
     constexpr int FN = BN / 64;                 // 32-row weight fragments per wave
     constexpr int FM = BM / 64;                 // 32-row activation fragments per wave
-    constexpr int DA = BN / 64;                 // DMA instructions per wave per stage, weights
-    constexpr int DB = BM / 64;                 // ... activations
+    constexpr int DA = BN / 32;                 // DMA instructions per wave per stage, weights
+    constexpr int DB = BM / 32;                 // ... activations
     constexpr int PER_STAGE = DA + DB;
-    constexpr int STAGE = (BN + BM) * kDK;
-    static_assert(STAGES >= 2 && STAGES <= 5, "stages");
-    __shared__ int sh[2];
+    constexpr int STAGE = (BN + BM) * kBK;
+    static_assert(STAGES == 2, "two-stage ring");
+    static_assert(BM * BN * 2 <= 2 * STAGE, "the BF16 output tile must fit in the ring");
+    int* sh = reinterpret_cast<int*>(smem + 2 * STAGE + 4 * (BN + BM));  // grouped tile lookup
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -162,16 +174,28 @@ __global__ __launch_bounds__(kThreadsM, 1) void gemm_mfma_kernel(MfmaArgs p) {
     // ---- output tile ------------------------------------------------------
     int tile_m, tile_n, expert = 0, row_begin = 0, rows_valid;
     if constexpr (!GROUPED) {
-        const int total = p.tiles_m * p.tiles_n;
+        // Workgroups are dealt round-robin to the 8 XCDs (blockIdx % 8).  When
+        // the tile grid splits evenly, XCD x owns a 2 x 4 block of the grid
+        // (half the activation tiles, a quarter of the weight tiles), so each
+        // XCD's L2 sees only its share of both operands; inside it, tiles go
+        // in groups of GROUP_M activation rows.
+        int sub_m = p.tiles_m, sub_n = p.tiles_n, off_m = 0, off_n = 0;
         int t = blockIdx.x;
-        if ((total & 7) == 0) t = (t & 7) * (total >> 3) + (t >> 3);  // XCD-contiguous
-        const int per_group = GROUP_M * p.tiles_n;
+        if ((p.tiles_m & 1) == 0 && (p.tiles_n & 3) == 0) {
+            const int x = t & 7;
+            t >>= 3;
+            sub_m = p.tiles_m >> 1;
+            sub_n = p.tiles_n >> 2;
+            off_m = (x >> 2) * sub_m;
+            off_n = (x & 3) * sub_n;
+        }
+        const int per_group = GROUP_M * sub_n;
         const int grp = t / per_group;
         const int first_m = grp * GROUP_M;
-        const int gsz = min(p.tiles_m - first_m, GROUP_M);
+        const int gsz = min(sub_m - first_m, GROUP_M);
         const int in = t - grp * per_group;
-        tile_m = first_m + in % gsz;
-        tile_n = in / gsz;
+        tile_m = off_m + first_m + in % gsz;
+        tile_n = off_n + in / gsz;
         rows_valid = p.M - tile_m * BM;
     } else {
         find_expert_tile<BM>(p, blockIdx.x, sh);
@@ -195,37 +219,50 @@ __global__ __launch_bounds__(kThreadsM, 1) void gemm_mfma_kernel(MfmaArgs p) {
         s_ch += (int64_t)expert * p.N;
     }
 
+    // ---- tile scales -> LDS (used by the epilogue) ------------------------
+    constexpr int RING = 2 * STAGE;
+    float* s_ch_t = reinterpret_cast<float*>(smem + RING);
+    float* s_tok_t = s_ch_t + BN;
+    for (int i = tid; i < BN; i += kThreadsM) s_ch_t[i] = s_ch[min(n0 + i, p.N - 1)];
+    for (int i = tid; i < BM; i += kThreadsM) {
+        const int ml = min(i, rows_valid - 1);
+        if constexpr (GROUPED)
+            s_tok_t[i] = p.s_tok[p.row_token[row_begin + m0 + ml]];
+        else
+            s_tok_t[i] = p.s_tok[m0 + ml];
+    }
+
     // ---- per-lane DMA sources ----------------------------------------------
-    // instruction j of this wave covers tile rows (wave * D + j) * 16 .. +15
-    const uint8_t* asrc[DA];
+    // Instruction j of this wave covers tile rows (wave * D + j) * 8 .. +7;
+    // lane l takes row l / 8 of those and the piece (l % 8) ^ swz(row).
+    const int lrow = lane >> 3;
+    const int lpos = lane & 7;
     const uint8_t* bsrc[DB];
 #pragma unroll
-    for (int j = 0; j < DA; ++j) {
-        const int row = (wave * DA + j) * 16 + (lane >> 2);
-        const int n = min(n0 + row, p.N - 1);  // rows past N feed discarded columns
-        asrc[j] = qw + (int64_t)n * ldw + (((lane & 3) ^ dswz(row)) << 4);
-    }
-#pragma unroll
     for (int j = 0; j < DB; ++j) {
-        const int row = (wave * DB + j) * 16 + (lane >> 2);
+        const int row = (wave * DB + j) * 8 + lrow;
         const int ml = min(row, rows_valid - 1);  // rows past the tile feed discarded rows
         int64_t src_row;
         if constexpr (GROUPED)
             src_row = p.row_token[row_begin + m0 + ml];
         else
             src_row = m0 + ml;
-        bsrc[j] = p.qa + src_row * lda + (((lane & 3) ^ dswz(row)) << 4);
+        bsrc[j] = p.qa + src_row * lda + ((lpos ^ dswz(row)) << 4);
     }
+    const int nlast = p.N - 1;
 
-    auto issue_stage = [&](int kt) {
-        uint8_t* base = smem + (kt % STAGES) * STAGE;
-        const int koff = kt * kDK;
+    // Stage kt goes to ring slot `slot` (0 or 1).
+    auto issue_stage = [&](int kt, int slot) {
+        uint8_t* base = smem + slot * STAGE;
+        const int koff = kt * kBK;
 #pragma unroll
-        for (int j = 0; j < DA; ++j)
-            dma16(asrc[j] + koff, base + (wave * DA + j) * 1024);
+        for (int j = 0; j < DA; ++j) {
+            const int row = (wave * DA + j) * 8 + lrow;
+            const int n = min(n0 + row, nlast);  // rows past N feed discarded columns
+            dma16(qw + (int64_t)n * ldw + koff + ((lpos ^ dswz(row)) << 4), base + (wave * DA + j) * 1024);
+        }
 #pragma unroll
-        for (int j = 0; j < DB; ++j)
-            dma16(bsrc[j] + koff, base + BN * kDK + (wave * DB + j) * 1024);
+        for (int j = 0; j < DB; ++j) dma16(bsrc[j] + koff, base + BN * kBK + (wave * DB + j) * 1024);
     };
 
     v16f acc[FN][FM];
@@ -236,80 +273,107 @@ __global__ __launch_bounds__(kThreadsM, 1) void gemm_mfma_kernel(MfmaArgs p) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
 
-    const int KT = p.K / kDK;
+    const int KT = p.K / kBK;
     const int arow0 = wn * (BN / 2) + r32;
     const int brow0 = wm * (BM / 2) + r32;
+    auto read_a = [&](int slot, int h, int a) { return read_frag(smem + slot * STAGE, arow0 + a * 32, h, g); };
+    auto read_b = [&](int slot, int h, int b) {
+        return read_frag(smem + slot * STAGE + BN * kBK, brow0 + b * 32, h, g);
+    };
+
     v8i fa[FN], fb[FM];
-
-    auto read_stage = [&](int kt, v8i (&ra)[FN], v8i (&rb)[FM]) {
-        const uint8_t* base = smem + (kt % STAGES) * STAGE;
-#pragma unroll
-        for (int b = 0; b < FM; ++b) rb[b] = read_frag(base + BN * kDK, brow0 + b * 32, g);
-#pragma unroll
-        for (int a = 0; a < FN; ++a) ra[a] = read_frag(base, arow0 + a * 32, g);
-    };
-    auto mma_stage = [&](const v8i (&ra)[FN], const v8i (&rb)[FM]) {
-#pragma unroll
-        for (int a = 0; a < FN; ++a)
-#pragma unroll
-            for (int b = 0; b < FM; ++b) acc[a][b] = mfma_32x32x64_e4m3(ra[a], rb[b], acc[a][b]);
-    };
-
-    // prologue: stages 0 .. STAGES-2 in flight
     if (KT > 0) {
-#pragma unroll
-        for (int s = 0; s < STAGES - 1; ++s)
-            if (s < KT) issue_stage(s);
-    }
-    for (int k = 0; k < KT; ++k) {
-        // this wave's DMA of stage k has landed; the barrier makes every
-        // wave's part visible and guarantees stage k-1 is no longer read
-        wait_dma<PER_STAGE>(min(KT - 1, k + STAGES - 2) - k);
+        // prologue: stages 0 and 1 in flight, stage 0 landed everywhere,
+        // its first-half fragments in registers
+        issue_stage(0, 0);
+        if (KT > 1) issue_stage(1, 1);
+        wait_dma<PER_STAGE>(KT > 1 ? 1 : 0);
         block_barrier();
-        if (k + STAGES - 1 < KT) issue_stage(k + STAGES - 1);  // into stage k-1's buffer
-        read_stage(k, fa, fb);
-        mma_stage(fa, fb);
-        wait_lds_reads();  // reads of stage k done before the next barrier
+#pragma unroll
+        for (int b = 0; b < FM; ++b) fb[b] = read_b(0, 0, b);
+#pragma unroll
+        for (int a = 0; a < FN; ++a) fa[a] = read_a(0, 0, a);
+    }
+    for (int s = 0; s < KT; ++s) {
+        const int cur = s & 1;
+        const bool more = s + 1 < KT;
+        // first K half of stage s; refill with the second half
+#pragma unroll
+        for (int a = 0; a < FN; ++a) {
+#pragma unroll
+            for (int b = 0; b < FM; ++b) {
+                acc[a][b] = mfma_32x32x64_e4m3(fa[a], fb[b], acc[a][b]);
+                if (a == FN - 1) fb[b] = read_b(cur, 1, b);
+            }
+            fa[a] = read_a(cur, 1, a);
+        }
+        if (more) {
+            wait_dma<PER_STAGE>(0);  // this wave's part of stage s+1 landed
+            wait_lds_reads();        // ... and its reads of stage s are done
+            block_barrier();
+            if (s + 2 < KT) issue_stage(s + 2, cur);
+        }
+        // second K half of stage s; refill with the first half of stage s+1
+        // (the last step re-reads its own slot, unused)
+        const int nxt = more ? cur ^ 1 : cur;
+#pragma unroll
+        for (int a = 0; a < FN; ++a) {
+#pragma unroll
+            for (int b = 0; b < FM; ++b) {
+                acc[a][b] = mfma_32x32x64_e4m3(fa[a], fb[b], acc[a][b]);
+                if (a == FN - 1) fb[b] = read_b(nxt, 0, b);
+            }
+            fa[a] = read_a(nxt, 0, a);
+        }
     }
 
     // ---- epilogue: y = bf16_rne(acc * (s_tok * s_ch)) ----------------------
-    // lane l of a 32x32 tile: column (activation row) l % 32, weight rows
-    // 8 * (v / 4) + 4 * (l / 32) + v % 4 for accumulator v.
-    const bool vec_store = GROUPED ? (p.N & 3) == 0 : (p.ldy & 3) == 0;
+    // The scaled BF16 tile is staged in LDS (the stage ring is free now) as
+    // [BM rows][BN columns] with 16-byte chunks XOR-swizzled by row, then
+    // written out with 16-byte row-contiguous stores.
+    // Accumulator layout of a 32x32 MFMA tile: lane l holds activation row
+    // l % 32 and weight columns 8 * (v / 4) + 4 * (l / 32) + v % 4, v = 0..15.
+    wait_lds_reads();
+    block_barrier();
+    uint8_t* ct = smem;
+    constexpr int CH = BN / 8;  // 16-byte chunks per tile row
 #pragma unroll
     for (int b = 0; b < FM; ++b) {
         const int ml = wm * (BM / 2) + b * 32 + r32;
-        if (ml >= rows_valid) continue;
-        int64_t yrow;
-        float st;
-        if constexpr (GROUPED) {
-            yrow = row_begin + m0 + ml;
-            st = p.s_tok[p.row_token[yrow]];
-        } else {
-            yrow = m0 + ml;
-            st = p.s_tok[yrow];
-        }
-        uint16_t* yr = p.y + yrow * (GROUPED ? (int64_t)p.N : p.ldy);
+        const float st = s_tok_t[ml];
 #pragma unroll
         for (int a = 0; a < FN; ++a) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int nb = n0 + wn * (BN / 2) + a * 32 + 8 * q + 4 * g;
-                if (nb >= p.N) continue;
-                const float c0 = acc[a][b][4 * q + 0], c1 = acc[a][b][4 * q + 1];
-                const float c2 = acc[a][b][4 * q + 2], c3 = acc[a][b][4 * q + 3];
-                if (nb + 3 < p.N && vec_store) {
-                    const float4 sc = *reinterpret_cast<const float4*>(s_ch + nb);
-                    uint2 o;
-                    o.x = pack_bf16x2(c0 * (st * sc.x), c1 * (st * sc.y));
-                    o.y = pack_bf16x2(c2 * (st * sc.z), c3 * (st * sc.w));
-                    *reinterpret_cast<uint2*>(yr + nb) = o;
-                } else {
-                    const float cv[4] = {c0, c1, c2, c3};
-                    for (int v = 0; v < 4 && nb + v < p.N; ++v)
-                        yr[nb + v] = (uint16_t)bf16_rne_bits(cv[v] * (st * s_ch[nb + v]));
-                }
+                const int nl = wn * (BN / 2) + a * 32 + 8 * q + 4 * g;
+                const float4 sc4 = *reinterpret_cast<const float4*>(s_ch_t + nl);
+                const float sc[4] = {sc4.x, sc4.y, sc4.z, sc4.w};
+                uint2 o;
+                o.x = pack_bf16x2(acc[a][b][4 * q + 0] * (st * sc[0]), acc[a][b][4 * q + 1] * (st * sc[1]));
+                o.y = pack_bf16x2(acc[a][b][4 * q + 2] * (st * sc[2]), acc[a][b][4 * q + 3] * (st * sc[3]));
+                const int chunk = (nl >> 3) ^ (ml & (CH - 1) & 31);
+                *reinterpret_cast<uint2*>(ct + ml * (BN * 2) + chunk * 16 + (nl & 7) * 2) = o;
             }
+        }
+    }
+    block_barrier();
+    const bool vec_store = GROUPED ? (p.N & 7) == 0 : (p.ldy & 7) == 0;
+    const int64_t ldy = GROUPED ? (int64_t)p.N : p.ldy;
+#pragma unroll 4
+    for (int id = tid; id < BM * CH; id += kThreadsM) {
+        const int row = id / CH, c = id % CH;
+        if (row >= rows_valid) continue;
+        const int n = n0 + c * 8;
+        if (n >= p.N) continue;
+        const int chunk = c ^ (row & (CH - 1) & 31);
+        const v4i val = *reinterpret_cast<const v4i*>(ct + row * (BN * 2) + chunk * 16);
+        const int64_t yrow = GROUPED ? (int64_t)row_begin + m0 + row : (int64_t)m0 + row;
+        uint16_t* dst = p.y + yrow * ldy + n;
+        if (vec_store && n + 8 <= p.N) {
+            *reinterpret_cast<v4i*>(dst) = val;
+        } else {
+            const uint16_t* h = reinterpret_cast<const uint16_t*>(&val);
+            for (int e = 0; e < 8 && n + e < p.N; ++e) dst[e] = h[e];
         }
     }
 }
@@ -322,8 +386,8 @@ hipError_t launch_gemm_mfma(const uint8_t* qa, int64_t lda, const float* s_tok, 
                             const float* s_ch, uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K,
                             hipStream_t stream) {
     if (M <= 0 || N <= 0) return hipSuccess;
-    constexpr int BN = 256, BM = 256, ST = 4;
-    constexpr int LDS = ST * (BN + BM) * kDK;
+    constexpr int BN = 256, BM = 256, ST = 2;
+    constexpr int LDS = ST * (BN + BM) * kBK + 4 * (BN + BM);  // ring + tile scales
     MfmaArgs p{};
     p.qa = qa; p.lda = lda; p.s_tok = s_tok; p.qw = qw; p.ldw = ldw; p.s_ch = s_ch; p.y = y; p.ldy = ldy;
     p.M = (int)M; p.N = (int)N; p.K = (int)K;
@@ -341,8 +405,8 @@ hipError_t launch_gemm_grouped_mfma(const uint8_t* qa, const float* s_tok, const
                                     int64_t T, int64_t R, int64_t E, int64_t N, int64_t K, hipStream_t stream) {
     (void)T;
     if (R <= 0 || N <= 0 || E <= 0) return hipSuccess;
-    constexpr int BN = 256, BM = 128, ST = 4;
-    constexpr int LDS = ST * (BN + BM) * kDK;
+    constexpr int BN = 256, BM = 128, ST = 2;
+    constexpr int LDS = ST * (BN + BM) * kBK + 4 * (BN + BM) + 16;  // ring + tile scales + tile lookup
     MfmaArgs p{};
     p.qa = qa; p.lda = K; p.s_tok = s_tok; p.qw = qw; p.ldw = K; p.s_ch = s_ch; p.y = y; p.ldy = N;
     p.M = (int)R; p.N = (int)N; p.K = (int)K;

@@ -25,12 +25,12 @@ hipError_t launch_gemm_tiled(const uint8_t* qa, int64_t lda, const float* s_tok,
                              int64_t ldw, const float* s_ch, uint16_t* y, int64_t ldy, int64_t M, int64_t N,
                              int64_t K, hipStream_t stream);
 
-// Multi-stage DMA-fed MFMA GEMM, K % 64 == 0 (gemm_mfma.hip).
+// Two-stage DMA-fed MFMA GEMM, K % 128 == 0 (gemm_mfma.hip).
 hipError_t launch_gemm_mfma(const uint8_t* qa, int64_t lda, const float* s_tok, const uint8_t* qw, int64_t ldw,
                             const float* s_ch, uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K,
                             hipStream_t stream);
 
-// Grouped (MoE) variant of the multi-stage kernel, K % 64 == 0 (gemm_mfma.hip).
+// Grouped (MoE) variant of the two-stage kernel, K % 128 == 0 (gemm_mfma.hip).
 hipError_t launch_gemm_grouped_mfma(const uint8_t* qa, const float* s_tok, const int32_t* row_token,
                                     const int32_t* offsets, const uint8_t* qw, const float* s_ch, uint16_t* y,
                                     int64_t T, int64_t R, int64_t E, int64_t N, int64_t K, hipStream_t stream);

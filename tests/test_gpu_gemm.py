@@ -36,7 +36,8 @@ def _gemm(qa, st, qw, sc):
 # M <= 64 runs the skinny kernel, larger M the tiled one; shapes span several
 # tiles with ragged M, N and K tails.
 SHAPES = [(1, 16, 16), (8, 200, 160), (16, 4096 + 48, 512), (33, 300, 1040), (64, 520, 2064),
-          (65, 272, 384), (200, 700, 1168), (513, 257, 2064), (300, 1024, 4096)]
+          (65, 272, 384), (200, 700, 1168), (513, 257, 2064), (300, 1024, 4096),
+          (129, 1000, 640), (777, 264, 1280), (256, 256, 128)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
