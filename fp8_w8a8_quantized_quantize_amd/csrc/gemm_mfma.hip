@@ -372,8 +372,9 @@ __global__ __launch_bounds__(kThreadsM, 1) void gemm_mfma_kernel(MfmaArgs p) {
         if (vec_store && n + 8 <= p.N) {
             *reinterpret_cast<v4i*>(dst) = val;
         } else {
-            const uint16_t* h = reinterpret_cast<const uint16_t*>(&val);
-            for (int e = 0; e < 8 && n + e < p.N; ++e) dst[e] = h[e];
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (n + e < p.N) dst[e] = (uint16_t)((uint32_t)val[e >> 1] >> ((e & 1) * 16));
         }
     }
 }
