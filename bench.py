@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU-oracle sample time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time eager launches instead of one HIP-graph replay of the steps")
     ap.add_argument("--profile", action="store_true",
                     help="few steps, no CPU baseline: for runs under rocprofv3")
     return ap.parse_args()
@@ -91,13 +93,35 @@ def gen_dense(w, seed):
     return x, wt
 
 
-def time_loop(fn, n, warmup):
-    """Run fn(i) warmup times, then n times between HIP events on the current
-    stream; returns (total ms, per-step ms list)."""
+def time_loop(fn, n, warmup, graph):
+    """Run fn(i) warmup times, then time n calls with HIP events on the stream
+    the library launches on (torch's current stream).  With graph=True the n
+    calls are captured once into a HIP graph and the timed region is one
+    replay, so host launch overhead is not part of the measurement (the
+    kernels and their on-GPU dispatch gaps are).  Returns (total ms,
+    per-step ms list or None)."""
     import torch
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn(0)  # warm the capture stream
+        torch.cuda.current_stream().wait_stream(side)
+        with torch.cuda.graph(g):
+            for i in range(n):
+                fn(i)
+        g.replay()  # untimed first replay
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1), None
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
     evs[0].record()
     for i in range(n):
@@ -166,6 +190,7 @@ def main():
     if args.profile:
         steps, warmup = min(steps, 10), min(warmup, 3)
     log = lambda *a: print(*a, file=sys.stderr, flush=True)
+    graph = not args.no_graph
 
     if w["kind"] == "dense":
         M, N, K = w["M"], w["N"], w["K"]
@@ -177,7 +202,8 @@ def main():
         wcopies = [wq] + [wq.clone() for _ in range(copies - 1)]
         xd = torch.from_numpy(x).to(dev)
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        ws = torch.empty(fp8.fp8_workspace_bytes(M, N, K), dtype=torch.uint8, device=dev)
+        # zero-filled once: the split-K counters inside are left zero by every call
+        ws = torch.zeros(max(1, fp8.fp8_workspace_bytes(M, N, K)), dtype=torch.uint8, device=dev)
         qa = torch.empty((M, K), dtype=torch.uint8, device=dev)
         st = torch.empty(M, dtype=torch.float32, device=dev)
 
@@ -188,11 +214,11 @@ def main():
         fp8.fp8_quantize_per_token(xd, q=qa, scales=st)
 
         def gemm(i):
-            fp8.fp8_gemm_scaled(qa, st, wcopies[i % copies], sc, y=y)
+            fp8.fp8_gemm_scaled(qa, st, wcopies[i % copies], sc, y=y, ws=ws)
 
         log(f"[bench] {copies} weight copies; warmup {warmup}, timing {steps} steps")
-        total_ms, per = time_loop(step, steps, warmup)
-        gemm_ms, gemm_per = time_loop(gemm, steps, warmup)
+        total_ms, per = time_loop(step, steps, warmup, graph)
+        gemm_ms, gemm_per = time_loop(gemm, steps, warmup, graph)
         ms = total_ms / steps
         decode = M <= 64
         flops = 2.0 * M * N * K
@@ -217,10 +243,12 @@ def main():
         roof["avg_launch_us"] = round(gemm_avg_ms * 1e3, 3)
         cfg = dict(workload=args.workload, M=M, N=N, K=K, seed=args.seed, weight_copies=copies,
                    step="fp8_quant_gemm_fused", out="bf16")
-        extra = dict(step_us_median=round(pct(per, 0.5) * 1e3, 3), step_us_p10=round(pct(per, 0.1) * 1e3, 3),
-                     step_us_p90=round(pct(per, 0.9) * 1e3, 3), step_tflops=round(flops / (ms * 1e-3) / 1e12, 2),
-                     step_gbs=round(step_bytes / (ms * 1e-3) / 1e9, 1),
-                     gemm_us_median=round(pct(gemm_per, 0.5) * 1e3, 3))
+        extra = dict(timing="hip-graph replay of the steps" if graph else "eager launches",
+                     step_us=round(ms * 1e3, 3), step_tflops=round(flops / (ms * 1e-3) / 1e12, 2),
+                     step_gbs=round(step_bytes / (ms * 1e-3) / 1e9, 1))
+        if per:
+            extra.update(step_us_median=round(pct(per, 0.5) * 1e3, 3), step_us_p10=round(pct(per, 0.1) * 1e3, 3),
+                         step_us_p90=round(pct(per, 0.9) * 1e3, 3), gemm_us_median=round(pct(gemm_per, 0.5) * 1e3, 3))
         cpu = None
         if not args.no_cpu_baseline and not args.profile:
             log("[bench] timing the CPU oracle")
@@ -255,8 +283,8 @@ def main():
         def gemm(i):
             fp8.fp8_gemm_grouped_scaled(qa, st, rtd, offd, qw, sc, y=y)
 
-        total_ms, per = time_loop(step, steps, warmup)
-        gemm_ms, gemm_per = time_loop(gemm, steps, warmup)
+        total_ms, per = time_loop(step, steps, warmup, graph)
+        gemm_ms, gemm_per = time_loop(gemm, steps, warmup, graph)
         ms = total_ms / steps
         flops = 2.0 * R * N * K
         gemm_bytes = E * N * K + 4 * E * N + T * K + 4 * T + 4 * R + 4 * (E + 1) + 2 * R * N
@@ -272,9 +300,11 @@ def main():
                     achieved_gbs=round(gemm_bytes / (gemm_avg_ms * 1e-3) / 1e9, 1))
         cfg = dict(workload=args.workload, T=T, E=E, topk=k, N=N, K=K, R=R, zipf=w["zipf"], seed=args.seed,
                    step="fp8_quantize_per_token + fp8_gemm_grouped_scaled", out="bf16")
-        extra = dict(step_us_median=round(pct(per, 0.5) * 1e3, 3), step_us_p10=round(pct(per, 0.1) * 1e3, 3),
-                     step_us_p90=round(pct(per, 0.9) * 1e3, 3), gemm_us_median=round(pct(gemm_per, 0.5) * 1e3, 3),
+        extra = dict(timing="hip-graph replay of the steps" if graph else "eager launches", step_us=round(ms * 1e3, 3),
                      expert_rows_max=int(np.diff(off).max()), expert_rows_min=int(np.diff(off).min()))
+        if per:
+            extra.update(step_us_median=round(pct(per, 0.5) * 1e3, 3), step_us_p10=round(pct(per, 0.1) * 1e3, 3),
+                         step_us_p90=round(pct(per, 0.9) * 1e3, 3), gemm_us_median=round(pct(gemm_per, 0.5) * 1e3, 3))
         cpu = None
         if not args.no_cpu_baseline and not args.profile:
             import oracle

@@ -10,6 +10,8 @@
 // Work split: a workgroup of KW waves owns NT x 16 weight rows; its waves take
 // interleaved 128-byte k chunks (wave w: chunks w, w+KW, ...) and are summed in
 // LDS in a fixed wave order at the end, so results are bit-reproducible.
+// Measured on MI355X: the activation fragments (re-read from L2 for every
+// 16 * NT weight rows) are what limits M = 64; larger NT cuts them.
 // MFMA A operand = 16 weight rows, B operand = 16 activation rows, so each
 // lane of the 16x16 result holds 4 consecutive output columns of one token
 // row (one 8-byte BF16 store).
@@ -135,31 +137,25 @@ __global__ __launch_bounds__(KW * 64) void gemm_skinny_kernel(
     }
 }
 
-template <int MT, int NT>
-static void launch_mt_nt(int depth, dim3 grid, hipStream_t stream, const uint8_t* qa, int64_t lda,
-                         const float* s_tok, const uint8_t* qw, int64_t ldw, const float* s_ch, uint16_t* y,
-                         int64_t ldy, int M, int N, int K) {
-    constexpr int KW = 4;
-    if (depth >= 4)
-        hipLaunchKernelGGL((gemm_skinny_kernel<MT, NT, KW, 4>), grid, dim3(KW * 64), 0, stream, qa, lda, s_tok, qw,
-                           ldw, s_ch, y, ldy, M, N, K);
-    else
-        hipLaunchKernelGGL((gemm_skinny_kernel<MT, NT, KW, 2>), grid, dim3(KW * 64), 0, stream, qa, lda, s_tok, qw,
-                           ldw, s_ch, y, ldy, M, N, K);
+template <int MT, int NT, int KW>
+static void launch_cfg(dim3 grid, hipStream_t stream, const uint8_t* qa, int64_t lda, const float* s_tok,
+                       const uint8_t* qw, int64_t ldw, const float* s_ch, uint16_t* y, int64_t ldy, int M, int N,
+                       int K) {
+    constexpr int DEPTH = (MT * NT <= 2) ? 4 : (MT * NT <= 16 ? 2 : 1);
+    hipLaunchKernelGGL((gemm_skinny_kernel<MT, NT, KW, DEPTH>), grid, dim3(KW * 64), 0, stream, qa, lda, s_tok, qw,
+                       ldw, s_ch, y, ldy, M, N, K);
 }
 
 template <int MT>
-static void launch_mt(int nt, int depth, hipStream_t stream, const uint8_t* qa, int64_t lda, const float* s_tok,
+static void launch_mt(int nt, dim3 grid, hipStream_t stream, const uint8_t* qa, int64_t lda, const float* s_tok,
                       const uint8_t* qw, int64_t ldw, const float* s_ch, uint16_t* y, int64_t ldy, int M, int N,
                       int K) {
-    const int rows = 16 * nt;
-    const dim3 grid((unsigned)((N + rows - 1) / rows));
-    if (nt == 4)
-        launch_mt_nt<MT, 4>(depth, grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, ldy, M, N, K);
-    else if (nt == 2)
-        launch_mt_nt<MT, 2>(depth, grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, ldy, M, N, K);
-    else
-        launch_mt_nt<MT, 1>(depth, grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, ldy, M, N, K);
+    switch (nt) {
+        case 8: launch_cfg<MT, 8, 4>(grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, ldy, M, N, K); break;
+        case 4: launch_cfg<MT, 4, 8>(grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, ldy, M, N, K); break;
+        case 2: launch_cfg<MT, 2, 8>(grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, ldy, M, N, K); break;
+        default: launch_cfg<MT, 1, 8>(grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, ldy, M, N, K); break;
+    }
 }
 
 hipError_t launch_gemm_skinny(const uint8_t* qa, int64_t lda, const float* s_tok, const uint8_t* qw,
@@ -167,17 +163,25 @@ hipError_t launch_gemm_skinny(const uint8_t* qa, int64_t lda, const float* s_tok
                               int64_t K, hipStream_t stream) {
     if (M <= 0 || N <= 0) return hipSuccess;
     const int mt = (int)((M + 15) / 16);
-    // Weight rows per workgroup: as many as keep >= ~1 workgroup per SIMD in flight.
+    // Weight rows per workgroup (16 * NT): as many as still leave >= 224
+    // workgroups (the activation fragments are re-read from L2 once per
+    // 16 * NT weight rows, so larger NT means less L2 traffic), up to 8 tiles
+    // when M needs 3-4 activation tiles and 4 otherwise.  Waves per
+    // workgroup that split K: 8, or 4 with NT = 8 (register budget).
+    const int nt_max = mt >= 3 ? 8 : 4;
     int nt = 1;
-    if ((N + 63) / 64 >= 448) nt = 4;
-    else if ((N + 31) / 32 >= 256) nt = 2;
-    const int depth = (mt + nt <= 4) ? 4 : 2;
+    for (int c = nt_max; c >= 1; c >>= 1)
+        if ((N + 16 * c - 1) / (16 * c) >= 224) {
+            nt = c;
+            break;
+        }
+    const dim3 grid((unsigned)((N + 16 * nt - 1) / (16 * nt)));
     const int m = (int)M, n = (int)N, k = (int)K;
     switch (mt) {
-        case 1: launch_mt<1>(nt, depth, stream, qa, lda, s_tok, qw, ldw, s_ch, y, ldy, m, n, k); break;
-        case 2: launch_mt<2>(nt, depth, stream, qa, lda, s_tok, qw, ldw, s_ch, y, ldy, m, n, k); break;
-        case 3: launch_mt<3>(nt, depth, stream, qa, lda, s_tok, qw, ldw, s_ch, y, ldy, m, n, k); break;
-        default: launch_mt<4>(nt, depth, stream, qa, lda, s_tok, qw, ldw, s_ch, y, ldy, m, n, k); break;
+        case 1: launch_mt<1>(nt, grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, ldy, m, n, k); break;
+        case 2: launch_mt<2>(nt, grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, ldy, m, n, k); break;
+        case 3: launch_mt<3>(nt, grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, ldy, m, n, k); break;
+        default: launch_mt<4>(nt, grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, ldy, m, n, k); break;
     }
     return hipGetLastError();
 }

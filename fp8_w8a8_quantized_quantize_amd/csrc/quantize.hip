@@ -1,8 +1,10 @@
 // Per-row absmax quantization to OCP E4M3 on gfx950.
 //
 // One row per workgroup of 256 threads (4 waves).  A row is read from HBM
-// once: short rows (K <= 16384) stay in registers between the absmax pass and
-// the cast pass; longer rows are re-read for the cast, from L2.  The absmax is
+// once: rows with K <= 32768 stay in registers between the absmax pass and
+// the cast pass (all of a row's loads are in flight at once, which is what
+// makes the few-row decode case fast); longer rows are re-read for the cast,
+// from L2.  The absmax is
 // a wave64 butterfly max (order independent, so it is exact) followed by a
 // 4-entry LDS reduction.  Scale and codes follow the Llama 3 FP8 page, §3.1:
 // s = max(fl32(amax / 448), 1e-12f), code = E4M3(fl32(x / s)) with an IEEE
@@ -102,6 +104,8 @@ hipError_t launch_quantize_rows(const float* x, int64_t ldx, uint8_t* q, int64_t
         hipLaunchKernelGGL(quantize_rows_regs<8>, dim3(grid), block, 0, stream, x, ldx, q, ldq, scales, rows, (int)K4);
     else if (K4 <= 256 * 16)
         hipLaunchKernelGGL(quantize_rows_regs<16>, dim3(grid), block, 0, stream, x, ldx, q, ldq, scales, rows, (int)K4);
+    else if (K4 <= 256 * 32)
+        hipLaunchKernelGGL(quantize_rows_regs<32>, dim3(grid), block, 0, stream, x, ldx, q, ldq, scales, rows, (int)K4);
     else
         hipLaunchKernelGGL(quantize_rows_loop, dim3(grid), block, 0, stream, x, ldx, q, ldq, scales, rows, K4);
     return hipGetLastError();
