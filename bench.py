@@ -41,7 +41,7 @@ DEFAULT_WORKLOAD = "llama3-8b-decode-up"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 KERNEL_SOURCES = {
     "skinny": ["gemm_skinny.hip", "device_common.hpp"],
-    "tiled": ["gemm_mfma.hip", "device_common.hpp"],
+    "mfma": ["gemm_mfma.hip", "device_common.hpp"],
 }
 
 
@@ -56,6 +56,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches instead of one HIP-graph replay of the steps")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run 5 plain device copies of 512 MiB (reference for rocprofv3 FETCH/WRITE_SIZE)")
     ap.add_argument("--profile", action="store_true",
                     help="few steps, no CPU baseline: for runs under rocprofv3")
     return ap.parse_args()
@@ -185,6 +187,14 @@ def main():
         sys.exit(3)
     fp8.lib()  # fail loudly if the HIP library is missing
     dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        src = torch.ones(512 << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "copy", "bytes_read": 512 << 20, "bytes_written": 512 << 20}))
+        return
     w = synth.WORKLOADS[args.workload]
     steps, warmup = args.steps, args.warmup
     if args.profile:
@@ -225,7 +235,7 @@ def main():
         step_bytes = 4 * M * K + N * K + 4 * N + 2 * M * N           # fused: fp32 x in, codes W, s_ch, bf16 y out
         gemm_bytes = M * K + 4 * M + N * K + 4 * N + 2 * M * N       # GEMM kernel: codes x, s_tok, W, s_ch, y
         gemm_avg_ms = gemm_ms / steps
-        kind = "skinny" if decode else "tiled"
+        kind = "skinny" if decode else "mfma"
         if decode:
             value, unit = step_bytes / (ms * 1e-3) / 1e9, "GB/s"
             achieved = gemm_bytes / (gemm_avg_ms * 1e-3) / 1e9
@@ -293,8 +303,8 @@ def main():
         achieved = flops / (gemm_avg_ms * 1e-3) / 1e12
         t_roof = max(flops / (FP8_PEAK_TFLOPS * 1e12), gemm_bytes / (HBM_PEAK_GBS * 1e9))
         roof = dict(bound="mfma", achieved=round(achieved, 1), peak=FP8_PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=round(achieved / FP8_PEAK_TFLOPS, 4), traffic=read_traffic(args.workload, "tiled"),
-                    kernel="gemm_tiled_kernel (grouped)", per_launch=f"{flops:.6g} FLOP",
+                    frac=round(achieved / FP8_PEAK_TFLOPS, 4), traffic=read_traffic(args.workload, "mfma"),
+                    kernel="gemm_mfma_kernel (grouped)", per_launch=f"{flops:.6g} FLOP",
                     avg_launch_us=round(gemm_avg_ms * 1e3, 3),
                     roofline_time_frac=round(t_roof / (gemm_avg_ms * 1e-3), 4),
                     achieved_gbs=round(gemm_bytes / (gemm_avg_ms * 1e-3) / 1e9, 1))
