@@ -17,6 +17,11 @@ namespace {
 
 constexpr int64_t kMaxDim = INT32_MAX;  // kernels index rows and columns with 32-bit ints
 constexpr size_t kAlign = 256;          // workspace sub-buffer alignment
+constexpr int64_t kMaxTiles = INT32_MAX - 8;  // launch grids count output tiles in 32 bits
+
+// Output tiles of 128 x 128 (no GEMM kernel uses smaller tiles along both axes
+// with one workgroup each), bounded so every grid and tile index fits 32 bits.
+bool tiles_ok(int64_t row_tiles, int64_t N) { return row_tiles * ((N + 127) / 128) <= kMaxTiles; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -33,6 +38,7 @@ fp8_status_t check_dims(int64_t M, int64_t N, int64_t K) {
     if (M < 0 || N < 0 || K < 0) return FP8_ERR_INVALID_ARGUMENT;
     if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return FP8_ERR_UNSUPPORTED;
     if (K % 16 != 0) return FP8_ERR_UNSUPPORTED;
+    if (!tiles_ok((M + 127) / 128, N)) return FP8_ERR_UNSUPPORTED;
     return FP8_OK;
 }
 
@@ -173,6 +179,7 @@ fp8_status_t fp8_gemm_grouped_scaled(const uint8_t* qa, const float* s_tok, cons
     FP8_TRY(check_dims(T, N, K));
     if (R < 0 || E < 0) return FP8_ERR_INVALID_ARGUMENT;
     if (R > kMaxDim || E > 1024) return FP8_ERR_UNSUPPORTED;
+    if (!tiles_ok((R + 127) / 128 + E, N)) return FP8_ERR_UNSUPPORTED;
     if (R > 0 && E == 0) return FP8_ERR_INVALID_ARGUMENT;
     if (R > 0 && T == 0) return FP8_ERR_INVALID_ARGUMENT;
     FP8_TRY(check_matrix(qa, T, K, K, 1));

@@ -114,20 +114,38 @@ struct MfmaArgs {
     int E;
 };
 
-// Expert owning grouped tile `tile` (prefix over experts of row tiles x
-// column tiles, computed by wave 0).  sh[0] = expert or -1, sh[1] = its first tile.
+// Number of output tiles of expert e (row tiles x column tiles).
 template <int BM>
-__device__ void find_expert_tile(const MfmaArgs& p, int tile, int* sh) {
+__device__ __forceinline__ int expert_tiles(const MfmaArgs& p, int e) {
+    const int rows = p.offsets[e + 1] - p.offsets[e];
+    return ((rows + BM - 1) / BM) * p.tiles_n;
+}
+
+// Grouped tile of workgroup b, computed by wave 0: sh[0] = expert (or -1 when
+// b has no tile), sh[1] = the tile's index inside that expert.
+//
+// The real tiles, numbered expert by expert, are cut into 8 contiguous ranges,
+// one per XCD (workgroups are dealt to the XCDs round-robin, b % 8), so the
+// tiles that share an expert's weights run side by side on one XCD and read
+// those weights through one L2.
+template <int BM>
+__device__ void find_expert_tile(const MfmaArgs& p, int b, int* sh) {
     if (threadIdx.x < 64) {
         const int lane = threadIdx.x;
-        int carry = 0, found_e = -1, found_base = 0;
+        int total = 0;
         for (int e0 = 0; e0 < p.E; e0 += 64) {
+            int cnt = (e0 + lane < p.E) ? expert_tiles<BM>(p, e0 + lane) : 0;
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off, 64);
+            total += cnt;
+        }
+        const int x = b & 7, j = b >> 3;
+        const int tile = (int)(((int64_t)x * total) >> 3) + j;
+        const int end = (int)(((int64_t)(x + 1) * total) >> 3);
+        int carry = 0, found_e = -1, found_local = 0;
+        for (int e0 = 0; e0 < p.E && tile < end; e0 += 64) {
             const int e = e0 + lane;
-            int cnt = 0;
-            if (e < p.E) {
-                const int rows = p.offsets[e + 1] - p.offsets[e];
-                cnt = ((rows + BM - 1) / BM) * p.tiles_n;
-            }
+            const int cnt = (e < p.E) ? expert_tiles<BM>(p, e) : 0;
             int incl = cnt;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
@@ -135,19 +153,19 @@ __device__ void find_expert_tile(const MfmaArgs& p, int tile, int* sh) {
                 if (lane >= off) incl += v;
             }
             const int excl = carry + incl - cnt;
-            const bool hit = (e < p.E) && cnt > 0 && tile >= excl && tile < excl + cnt;
+            const bool hit = cnt > 0 && tile >= excl && tile < excl + cnt;
             const unsigned long long mask = __ballot(hit);
             if (mask) {
                 const int src = __ffsll((long long)mask) - 1;
                 found_e = __shfl(e, src, 64);
-                found_base = __shfl(excl, src, 64);
+                found_local = tile - __shfl(excl, src, 64);
                 break;
             }
             carry += __shfl(incl, 63, 64);
         }
         if (lane == 0) {
             sh[0] = found_e;
-            sh[1] = found_base;
+            sh[1] = found_local;
         }
     }
     __syncthreads();
@@ -200,13 +218,19 @@ __global__ __launch_bounds__(kThreadsM, 1) void gemm_mfma_kernel(MfmaArgs p) {
     } else {
         find_expert_tile<BM>(p, blockIdx.x, sh);
         expert = sh[0];
-        if (expert < 0) return;  // past the last tile (uniform over the block)
-        const int local = blockIdx.x - sh[1];
+        if (expert < 0) return;  // no tile for this workgroup (uniform over the block)
+        const int local = sh[1];
         row_begin = p.offsets[expert];
         const int rows_e = p.offsets[expert + 1] - row_begin;
         const int mt_e = (rows_e + BM - 1) / BM;
-        tile_m = local % mt_e;
-        tile_n = local / mt_e;
+        // inside the expert: groups of GROUP_M row tiles, row tiles fastest
+        const int per_group = GROUP_M * p.tiles_n;
+        const int grp = local / per_group;
+        const int first_m = grp * GROUP_M;
+        const int gsz = min(mt_e - first_m, GROUP_M);
+        const int in = local - grp * per_group;
+        tile_m = first_m + in % gsz;
+        tile_n = in / gsz;
         rows_valid = rows_e - tile_m * BM;
     }
     const int n0 = tile_n * BN;
@@ -406,17 +430,21 @@ hipError_t launch_gemm_grouped_mfma(const uint8_t* qa, const float* s_tok, const
                                     int64_t T, int64_t R, int64_t E, int64_t N, int64_t K, hipStream_t stream) {
     (void)T;
     if (R <= 0 || N <= 0 || E <= 0) return hipSuccess;
-    constexpr int BN = 256, BM = 128, ST = 2;
+    constexpr int BN = 256, BM = 256, ST = 2;
     constexpr int LDS = ST * (BN + BM) * kBK + 4 * (BN + BM) + 16;  // ring + tile scales + tile lookup
     MfmaArgs p{};
     p.qa = qa; p.lda = K; p.s_tok = s_tok; p.qw = qw; p.ldw = K; p.s_ch = s_ch; p.y = y; p.ldy = N;
     p.M = (int)R; p.N = (int)N; p.K = (int)K;
     p.tiles_n = (int)((N + BN - 1) / BN);
     p.row_token = row_token; p.offsets = offsets; p.E = (int)E;
-    hipError_t e = FP8K_SET_LDS((gemm_mfma_kernel<BN, BM, ST, 1, true>), LDS);
+    constexpr int GM = 4;
+    hipError_t e = FP8K_SET_LDS((gemm_mfma_kernel<BN, BM, ST, GM, true>), LDS);
     if (e != hipSuccess) return e;
-    const int64_t grid = ((R + BM - 1) / BM + E) * p.tiles_n;
-    hipLaunchKernelGGL((gemm_mfma_kernel<BN, BM, ST, 1, true>), dim3((unsigned)grid), dim3(kThreadsM), LDS, stream, p);
+    // sum over experts of ceil(rows_e / BM) <= ceil(R / BM) + E; each of the 8
+    // XCD ranges holds at most ceil(total / 8) tiles
+    const int64_t tiles_max = ((R + BM - 1) / BM + E) * p.tiles_n;
+    const int64_t grid = 8 * ((tiles_max + 7) / 8);
+    hipLaunchKernelGGL((gemm_mfma_kernel<BN, BM, ST, GM, true>), dim3((unsigned)grid), dim3(kThreadsM), LDS, stream, p);
     return hipGetLastError();
 }
 

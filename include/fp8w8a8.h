@@ -33,7 +33,11 @@
  *                                 negative extent, leading dimension below the
  *                                 row length, or a size that overflows int64;
  *       FP8_ERR_UNSUPPORTED       K not a multiple of 16, an extent above
- *                                 2^31 - 1, a pointer not 16-byte aligned, or
+ *                                 2^31 - 1, an output with more than
+ *                                 2^31 - 9 tiles of 128 x 128 (for the
+ *                                 grouped GEMM: (ceil(R/128) + E) row tiles
+ *                                 times ceil(N/128)), a pointer not 16-byte
+ *                                 aligned, or
  *                                 an input row stride (x, qa, qw) that is not
  *                                 a multiple of 16 bytes (y may have any
  *                                 row stride ldy >= N);

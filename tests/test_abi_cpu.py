@@ -101,6 +101,8 @@ def test_gemm_validation():
     assert with_(y=0) == FP8_ERR_INVALID_ARGUMENT
     assert with_(s_ch=MIS) == FP8_ERR_UNSUPPORTED
     assert with_(M=-3) == FP8_ERR_INVALID_ARGUMENT
+    # 2^23 x 2^23 output tiles of 128 x 128 do not fit a 32-bit launch grid
+    assert with_(M=1 << 30, N=1 << 30, ldy=1 << 30) == FP8_ERR_UNSUPPORTED
     assert with_(M=0, qa=0, s_tok=0, y=0) == FP8_OK       # empty: no-op
     assert with_(N=0, qw=0, s_ch=0, y=0) == FP8_OK
 
@@ -156,6 +158,7 @@ def test_grouped_validation():
     assert with_(qw=0) == FP8_ERR_INVALID_ARGUMENT
     assert with_(sc=MIS) == FP8_ERR_UNSUPPORTED
     assert with_(R=-1) == FP8_ERR_INVALID_ARGUMENT
+    assert with_(R=1 << 30, N=1 << 30) == FP8_ERR_UNSUPPORTED   # tile grid beyond 32 bits
     assert with_(R=0, rt=0, off=0, y=0) == FP8_OK
 
 
