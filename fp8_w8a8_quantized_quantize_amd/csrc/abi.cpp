@@ -163,6 +163,9 @@ fp8_status_t fp8_quant_gemm_fused(const float* x, int64_t ldx, const uint8_t* qw
     if (need > 0 && ws == nullptr) return FP8_ERR_INVALID_ARGUMENT;
     if (need > 0 && !aligned16(ws)) return FP8_ERR_UNSUPPORTED;
     if (M == 0) return FP8_OK;
+    if (N > 0 && fp8k::gemm_skinny_fused_fits(M, K))
+        return from_hip(fp8k::launch_gemm_skinny_fused(x, ldx, qw, ldw, s_ch, y, ldy, M, N, K, qa_out, s_tok_out,
+                                                       stream));
     uint8_t* base = static_cast<uint8_t*>(ws);
     uint8_t* qa = qa_out ? qa_out : base;
     float* s_tok = s_tok_out ? s_tok_out : reinterpret_cast<float*>(base + round_up((size_t)M * (size_t)K, kAlign));

@@ -69,6 +69,50 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
+// Per-token quantization steps shared by the quantizer and the fused decode
+// GEMM (Llama 3 FP8 page, §3.1): running |x| maximum, the row scale
+// s = max(fl32(amax / 448), 1e-12f) and the codes E4M3(fl32(x / s)).
+__device__ __forceinline__ float absmax4(float m, const float4& v) {
+    return fmaxf(fmaxf(m, fmaxf(fabsf(v.x), fabsf(v.y))), fmaxf(fabsf(v.z), fabsf(v.w)));
+}
+
+__device__ __forceinline__ float row_scale(float amax) {
+    float s = __fdiv_rn(amax, kE4M3Max);
+    return s < kScaleFloor ? kScaleFloor : s;
+}
+
+// A row's scale and its correctly rounded reciprocal.
+struct RowScale {
+    float s, r;
+};
+
+__device__ __forceinline__ RowScale make_row_scale(float amax) {
+    const float s = row_scale(amax);
+    return RowScale{s, __fdiv_rn(1.0f, s)};
+}
+
+// fl32(x / s) from r = RN(1 / s): q0 = RN(x r) is within one ulp of x / s,
+// the residual x - q0 s is exact in one FMA, and RN(q0 + residual * r) is
+// then the correctly rounded quotient (Markstein's division theorem; a
+// reciprocal and two FMAs instead of a full IEEE division per element).  The
+// sign of x is put back so -0 stays -0.  Where x is subnormal the residual
+// can lose bits, but the quotient is then below 2^-11, whose E4M3 code is the
+// signed zero either way.  A CPU test checks this against IEEE division on
+// random and on E4M3-boundary quotients.
+__device__ __forceinline__ float div_by_scale(float x, const RowScale& rs) {
+    const float q0 = x * rs.r;
+    const float e = __builtin_fmaf(-q0, rs.s, x);
+    return __builtin_copysignf(__builtin_fmaf(e, rs.r, q0), x);
+}
+
+__device__ __forceinline__ uint32_t cast4(const float4& v, const RowScale& rs) {
+    return cvt4_e4m3(div_by_scale(v.x, rs), div_by_scale(v.y, rs), div_by_scale(v.z, rs), div_by_scale(v.w, rs));
+}
+
 __device__ __forceinline__ v4i load16(const uint8_t* p) { return *reinterpret_cast<const v4i*>(p); }
+
+// Kernels that take more than 64 KB of dynamic LDS need this opt-in before launch.
+#define FP8K_SET_LDS(KERNEL, BYTES) \
+    hipFuncSetAttribute(reinterpret_cast<const void*>(&KERNEL), hipFuncAttributeMaxDynamicSharedMemorySize, (BYTES))
 
 }  // namespace fp8k

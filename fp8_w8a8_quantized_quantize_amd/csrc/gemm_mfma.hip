@@ -403,10 +403,6 @@ __global__ __launch_bounds__(kThreadsM, 1) void gemm_mfma_kernel(MfmaArgs p) {
     }
 }
 
-// The kernels use more than 64 KB of dynamic LDS, which needs an opt-in.
-#define FP8K_SET_LDS(KERNEL, BYTES) \
-    hipFuncSetAttribute(reinterpret_cast<const void*>(&KERNEL), hipFuncAttributeMaxDynamicSharedMemorySize, (BYTES))
-
 hipError_t launch_gemm_mfma(const uint8_t* qa, int64_t lda, const float* s_tok, const uint8_t* qw, int64_t ldw,
                             const float* s_ch, uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K,
                             hipStream_t stream) {

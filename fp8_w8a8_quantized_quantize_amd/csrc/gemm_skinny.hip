@@ -20,6 +20,13 @@
 
 namespace fp8k {
 
+// Keeps the compiler's scheduler from moving any instruction across this
+// point: each step's loads are issued right after the step they replace is
+// consumed, in program order (the order they return in), and the next step's
+// operand selects cannot be hoisted above this step's MFMAs (a hoisted select
+// would wait for loads that are meant to stay in flight).
+__device__ __forceinline__ void issue_order_fence() { __builtin_amdgcn_sched_barrier(0); }
+
 // Lane `lane` supplies bytes [16g, 16g+16) and [64+16g, 64+16g+16) of a
 // 128-byte k chunk (g = lane / 16) for A and B alike.
 template <int MT, int NT, int KW, int DEPTH>
@@ -36,20 +43,16 @@ __global__ __launch_bounds__(KW * 64) void gemm_skinny_kernel(
     const int steps = nchunks > wave ? (nchunks - wave + KW - 1) / KW : 0;
 
     const uint8_t* wrow[NT];
-    bool wok[NT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
         const int n = n0 + 16 * j + r16;
-        wok[j] = n < N;
-        wrow[j] = qw + (int64_t)(wok[j] ? n : 0) * ldw;
+        wrow[j] = qw + (int64_t)(n < N ? n : 0) * ldw;
     }
     const uint8_t* xrow[MT];
-    bool xok[MT];
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
         const int m = 16 * i + r16;
-        xok[i] = m < M;
-        xrow[i] = qa + (int64_t)(xok[i] ? m : 0) * lda;
+        xrow[i] = qa + (int64_t)(m < M ? m : 0) * lda;
     }
 
     v4f acc[MT][NT];
@@ -62,46 +65,54 @@ __global__ __launch_bounds__(KW * 64) void gemm_skinny_kernel(
     v4i xb[DEPTH][MT][2];
     const v4i zero = v4i{0, 0, 0, 0};
 
+    // Loads are issued raw and consumed DEPTH steps later; the operand
+    // selects that zero a partial last k chunk happen at the point of use and
+    // a scheduling barrier closes every step, so the compiler waits for exactly
+    // the loads of the step being consumed while the next DEPTH - 1 steps stay
+    // in flight (vector loads return in order: a select hoisted next to a load
+    // would make the wave wait for everything issued before it).  Offsets past
+    // K read the row's first bytes (K >= 16 whenever a step runs).  Rows past
+    // N or M read row 0: they only feed output elements that are never stored.
     auto load_step = [&](int s, v4i (&wd)[NT][2], v4i (&xd)[MT][2]) {
         const int kb = (wave + KW * s) * 128;
-        const bool ok0 = kb + 16 * g < K;
-        const bool ok1 = kb + 64 + 16 * g < K;
-        // out-of-range chunks read the row's first 16 bytes (K >= 16 whenever
-        // a step runs) and are replaced by zeros
-        const int o0 = ok0 ? kb + 16 * g : 0;
-        const int o1 = ok1 ? kb + 64 + 16 * g : 0;
+        const int o0 = kb + 16 * g < K ? kb + 16 * g : 0;
+        const int o1 = kb + 64 + 16 * g < K ? kb + 64 + 16 * g : 0;
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
-            v4i a = load16(wrow[j] + o0);
-            v4i b = load16(wrow[j] + o1);
-            wd[j][0] = (ok0 && wok[j]) ? a : zero;
-            wd[j][1] = (ok1 && wok[j]) ? b : zero;
+            wd[j][0] = load16(wrow[j] + o0);
+            wd[j][1] = load16(wrow[j] + o1);
         }
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
-            v4i a = load16(xrow[i] + o0);
-            v4i b = load16(xrow[i] + o1);
-            xd[i][0] = (ok0 && xok[i]) ? a : zero;
-            xd[i][1] = (ok1 && xok[i]) ? b : zero;
+            xd[i][0] = load16(xrow[i] + o0);
+            xd[i][1] = load16(xrow[i] + o1);
         }
     };
 
+    if (steps > 0) {
+        // (unconditional, so the compiler knows the return order exactly;
+        // steps beyond the last repeat it and are never consumed)
 #pragma unroll
-    for (int d = 0; d < DEPTH; ++d)
-        if (d < steps) load_step(d, wb[d], xb[d]);
-
-    for (int s0 = 0; s0 < steps; s0 += DEPTH) {
+        for (int d = 0; d < DEPTH; ++d) load_step(min(d, steps - 1), wb[d], xb[d]);
+        issue_order_fence();
+        for (int s0 = 0; s0 < steps; s0 += DEPTH) {
 #pragma unroll
-        for (int d = 0; d < DEPTH; ++d) {
-            const int s = s0 + d;
-            if (s < steps) {
+            for (int d = 0; d < DEPTH; ++d) {
+                const int s = s0 + d;
+                const int kb = (wave + KW * s) * 128;
+                const bool ok0 = s < steps && kb + 16 * g < K;
+                const bool ok1 = s < steps && kb + 64 + 16 * g < K;
+                v8i xf[MT];
+#pragma unroll
+                for (int i = 0; i < MT; ++i) xf[i] = join(ok0 ? xb[d][i][0] : zero, ok1 ? xb[d][i][1] : zero);
 #pragma unroll
                 for (int j = 0; j < NT; ++j) {
-                    const v8i a = join(wb[d][j][0], wb[d][j][1]);
+                    const v8i a = join(ok0 ? wb[d][j][0] : zero, ok1 ? wb[d][j][1] : zero);
 #pragma unroll
-                    for (int i = 0; i < MT; ++i) acc[i][j] = mfma_16x16x128_e4m3(a, join(xb[d][i][0], xb[d][i][1]), acc[i][j]);
+                    for (int i = 0; i < MT; ++i) acc[i][j] = mfma_16x16x128_e4m3(a, xf[i], acc[i][j]);
                 }
                 if (s + DEPTH < steps) load_step(s + DEPTH, wb[d], xb[d]);
+                issue_order_fence();
             }
         }
     }
@@ -137,11 +148,184 @@ __global__ __launch_bounds__(KW * 64) void gemm_skinny_kernel(
     }
 }
 
+// Fused per-token quantization + skinny GEMM for a few rows whose codes fit in
+// LDS and whose fp32 values fit in 16 float4 registers per lane: M <= 8 rows
+// of K <= 4096 (wave w holds row w) or M <= 16 rows of K <= 2048 (wave w holds
+// rows w and w + 8).  Every workgroup issues its loads of x first and its
+// first DEPTH steps of weight loads right after them (vector loads complete in
+// issue order, so the quantization can start while the weight stream is in
+// flight), quantizes the whole activation matrix itself exactly as the
+// stand-alone quantizer does, into an LDS copy of the codes, and then runs the
+// weight-streaming loop above with the activation fragments read from LDS.
+// Workgroup 0 also writes the codes and scales to qa_out / s_tok_out when
+// those are given.
+constexpr int kFusedRowPad = 16;          // bytes after each LDS code row (bank spread)
+constexpr int kFusedRegVec = 16;          // float4 registers per lane for x
+constexpr int kFusedWaves = 8;
+
+template <int NT, int KW, int DEPTH>
+__global__ __launch_bounds__(KW * 64) void gemm_skinny_fused_kernel(
+    const float* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ qw, int64_t ldw,
+    const float* __restrict__ s_ch, uint16_t* __restrict__ y, int64_t ldy, int M, int N, int K,
+    uint8_t* __restrict__ qa_out, float* __restrict__ s_tok_out) {
+    extern __shared__ __align__(16) uint8_t fused_smem[];
+    __shared__ float s_tok_sh[16];
+    __shared__ v4f red[KW][NT][64];
+    static_assert(KW == kFusedWaves, "one or two rows per wave cover M <= 16");
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int r16 = lane & 15;
+    const int g = lane >> 4;
+    const int n0 = blockIdx.x * (NT * 16);
+    const int nchunks = (K + 127) >> 7;
+    const int steps = nchunks > wave ? (nchunks - wave + KW - 1) / KW : 0;
+    const int ldq = K + kFusedRowPad;
+    uint8_t* xq = fused_smem;
+
+    // ---- x loads, then the first weight steps.  Everything up to the first
+    // use of x is unconditional (indexes are clamped instead), so the compiler
+    // knows that the x loads return first and waits for them alone.
+    // Register e holds row wave + KW * slot(e), float4 index lane + 64 * idx(e):
+    // one row per wave: slot = 0, idx = e; two rows: slot = e / 8, idx = e % 8.
+    // A wave without a row, or an index past the row, re-reads a valid float4
+    // that is then ignored.
+    const int K4 = K >> 2;
+    const bool two = M > KW;
+    const uint8_t* wrow[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        const int n = n0 + 16 * j + r16;
+        wrow[j] = qw + (int64_t)(n < N ? n : 0) * ldw;
+    }
+    v4f acc[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
+    v4i wb[DEPTH][NT][2];
+    const v4i zero = v4i{0, 0, 0, 0};
+    auto load_w = [&](int s, v4i (&wd)[NT][2]) {
+        const int kb = (wave + KW * s) * 128;
+        const int o0 = kb + 16 * g < K ? kb + 16 * g : 0;
+        const int o1 = kb + 64 + 16 * g < K ? kb + 64 + 16 * g : 0;
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            wd[j][0] = load16(wrow[j] + o0);
+            wd[j][1] = load16(wrow[j] + o1);
+        }
+    };
+
+    RowScale sc0 = make_row_scale(0.0f), sc1 = sc0;  // K == 0: the scale is the floor
+    if (K4 > 0) {
+        float4 v[kFusedRegVec];
+#pragma unroll
+        for (int e = 0; e < kFusedRegVec; ++e) {
+            const int slot = two ? (e >> 3) : 0;
+            const int idx = two ? (e & 7) : e;
+            const int mr = wave + KW * slot;
+            const int m = mr < M ? mr : 0;
+            const int j = min(lane + 64 * idx, K4 - 1);
+            v[e] = reinterpret_cast<const float4*>(x + (int64_t)m * ldx)[j];
+        }
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) load_w(d, wb[d]);  // past the last step: never consumed
+        issue_order_fence();
+
+        // ---- quantize x into LDS
+        float amax0 = 0.0f, amax1 = 0.0f;
+#pragma unroll
+        for (int e = 0; e < kFusedRegVec; ++e) {
+            const bool second = two && e >= 8;
+            const int idx = two ? (e & 7) : e;
+            const bool ok = wave + (second ? KW : 0) < M && lane + 64 * idx < K4;
+            const float a = absmax4(0.0f, v[e]);
+            if (second)
+                amax1 = fmaxf(amax1, ok ? a : 0.0f);
+            else
+                amax0 = fmaxf(amax0, ok ? a : 0.0f);
+        }
+        sc0 = make_row_scale(wave_max(amax0));
+        sc1 = make_row_scale(wave_max(amax1));
+        const bool keep = blockIdx.x == 0;
+#pragma unroll
+        for (int e = 0; e < kFusedRegVec; ++e) {
+            const bool second = two && e >= 8;
+            const int idx = two ? (e & 7) : e;
+            const int m = wave + (second ? KW : 0);
+            const int j = lane + 64 * idx;
+            if (m < M && j < K4) {
+                const uint32_t c = cast4(v[e], second ? sc1 : sc0);
+                reinterpret_cast<uint32_t*>(xq + m * ldq)[j] = c;
+                if (keep && qa_out) reinterpret_cast<uint32_t*>(qa_out + (int64_t)m * K)[j] = c;
+            }
+        }
+    }
+    if (lane == 0) {
+        const bool keep = blockIdx.x == 0 && s_tok_out != nullptr;
+        if (wave < M) {
+            s_tok_sh[wave] = sc0.s;
+            if (keep) s_tok_out[wave] = sc0.s;
+        }
+        if (wave + KW < M) {
+            s_tok_sh[wave + KW] = sc1.s;
+            if (keep) s_tok_out[wave + KW] = sc1.s;
+        }
+    }
+    __syncthreads();
+
+    // ---- weight stream, activation fragments from LDS -----------------------
+    // (rows past M read row 0 of the LDS copy: their outputs are never stored;
+    // offsets past K read the row start and are zeroed)
+    const uint8_t* xs = xq + (r16 < M ? r16 : 0) * ldq;
+    if (steps > 0) {
+        for (int s0 = 0; s0 < steps; s0 += DEPTH) {
+#pragma unroll
+            for (int d = 0; d < DEPTH; ++d) {
+                const int s = s0 + d;
+                const int kb = (wave + KW * s) * 128;
+                const bool ok0 = s < steps && kb + 16 * g < K;
+                const bool ok1 = s < steps && kb + 64 + 16 * g < K;
+                const v4i xa = *reinterpret_cast<const v4i*>(xs + (ok0 ? kb + 16 * g : 0));
+                const v4i xc = *reinterpret_cast<const v4i*>(xs + (ok1 ? kb + 64 + 16 * g : 0));
+                const v8i b = join(ok0 ? xa : zero, ok1 ? xc : zero);
+#pragma unroll
+                for (int j = 0; j < NT; ++j)
+                    acc[j] = mfma_16x16x128_e4m3(join(ok0 ? wb[d][j][0] : zero, ok1 ? wb[d][j][1] : zero), b, acc[j]);
+                if (s + DEPTH < steps) load_w(s + DEPTH, wb[d]);
+                issue_order_fence();
+            }
+        }
+    }
+
+    // ---- sum the KW partial tiles in wave order, scale, store ---------------
+#pragma unroll
+    for (int j = 0; j < NT; ++j) red[wave][j][lane] = acc[j];
+    __syncthreads();
+    for (int j = wave; j < NT; j += KW) {
+        v4f sum = red[0][j][lane];
+#pragma unroll
+        for (int w = 1; w < KW; ++w) sum += red[w][j][lane];
+        const int m = r16;
+        const int nb = n0 + 16 * j + 4 * g;
+        if (m >= M || nb >= N) continue;
+        const float st = s_tok_sh[m];
+        uint16_t* yr = y + (int64_t)m * ldy;
+        if (nb + 3 < N && (ldy & 3) == 0) {
+            const float4 sc = *reinterpret_cast<const float4*>(s_ch + nb);
+            uint2 o;
+            o.x = pack_bf16x2(sum[0] * (st * sc.x), sum[1] * (st * sc.y));
+            o.y = pack_bf16x2(sum[2] * (st * sc.z), sum[3] * (st * sc.w));
+            *reinterpret_cast<uint2*>(yr + nb) = o;
+        } else {
+            for (int v = 0; v < 4 && nb + v < N; ++v)
+                yr[nb + v] = (uint16_t)bf16_rne_bits(sum[v] * (st * s_ch[nb + v]));
+        }
+    }
+}
+
 template <int MT, int NT, int KW>
 static void launch_cfg(dim3 grid, hipStream_t stream, const uint8_t* qa, int64_t lda, const float* s_tok,
                        const uint8_t* qw, int64_t ldw, const float* s_ch, uint16_t* y, int64_t ldy, int M, int N,
                        int K) {
-    constexpr int DEPTH = (MT * NT <= 2) ? 4 : (MT * NT <= 16 ? 2 : 1);
+    constexpr int DEPTH = (MT * NT <= 2) ? 4 : 2;
     hipLaunchKernelGGL((gemm_skinny_kernel<MT, NT, KW, DEPTH>), grid, dim3(KW * 64), 0, stream, qa, lda, s_tok, qw,
                        ldw, s_ch, y, ldy, M, N, K);
 }
@@ -184,6 +368,46 @@ hipError_t launch_gemm_skinny(const uint8_t* qa, int64_t lda, const float* s_tok
         default: launch_mt<4>(nt, grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, ldy, m, n, k); break;
     }
     return hipGetLastError();
+}
+
+bool gemm_skinny_fused_fits(int64_t M, int64_t K) {
+    if (M < 1 || M > kSkinnyFusedMaxM || M * (K + kFusedRowPad) > kSkinnyFusedLds) return false;
+    const int64_t vec_per_row = (K / 4 + 63) / 64;
+    return vec_per_row <= (M > kFusedWaves ? kFusedRegVec / 2 : kFusedRegVec);
+}
+
+template <int NT, int KW>
+static hipError_t launch_fused_cfg(dim3 grid, size_t lds, hipStream_t stream, const float* x, int64_t ldx,
+                             const uint8_t* qw, int64_t ldw, const float* s_ch, uint16_t* y, int64_t ldy, int M,
+                             int N, int K, uint8_t* qa_out, float* s_tok_out) {
+    constexpr int DEPTH = NT <= 2 ? 4 : 2;
+    const hipError_t e = FP8K_SET_LDS((gemm_skinny_fused_kernel<NT, KW, DEPTH>), (int)kSkinnyFusedLds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((gemm_skinny_fused_kernel<NT, KW, DEPTH>), grid, dim3(KW * 64), lds, stream, x, ldx, qw, ldw,
+                       s_ch, y, ldy, M, N, K, qa_out, s_tok_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_skinny_fused(const float* x, int64_t ldx, const uint8_t* qw, int64_t ldw, const float* s_ch,
+                                    uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K, uint8_t* qa_out,
+                                    float* s_tok_out, hipStream_t stream) {
+    if (M <= 0 || N <= 0) return hipSuccess;
+    if (!gemm_skinny_fused_fits(M, K)) return hipErrorInvalidValue;
+    // the same weight-rows-per-workgroup rule as the unfused M <= 16 case
+    int nt = 1;
+    for (int c = 4; c >= 1; c >>= 1)
+        if ((N + 16 * c - 1) / (16 * c) >= 224) {
+            nt = c;
+            break;
+        }
+    const dim3 grid((unsigned)((N + 16 * nt - 1) / (16 * nt)));
+    const size_t lds = (size_t)(M * (K + kFusedRowPad));
+    const int m = (int)M, n = (int)N, k = (int)K;
+    switch (nt) {
+        case 4: return launch_fused_cfg<4, 8>(grid, lds, stream, x, ldx, qw, ldw, s_ch, y, ldy, m, n, k, qa_out, s_tok_out);
+        case 2: return launch_fused_cfg<2, 8>(grid, lds, stream, x, ldx, qw, ldw, s_ch, y, ldy, m, n, k, qa_out, s_tok_out);
+        default: return launch_fused_cfg<1, 8>(grid, lds, stream, x, ldx, qw, ldw, s_ch, y, ldy, m, n, k, qa_out, s_tok_out);
+    }
 }
 
 }  // namespace fp8k

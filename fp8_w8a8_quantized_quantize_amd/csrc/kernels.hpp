@@ -20,6 +20,16 @@ hipError_t launch_gemm_skinny(const uint8_t* qa, int64_t lda, const float* s_tok
                               int64_t ldw, const float* s_ch, uint16_t* y, int64_t ldy, int64_t M, int64_t N,
                               int64_t K, hipStream_t stream);
 
+// Quantize + skinny GEMM in one kernel, for M <= kSkinnyFusedMaxM rows whose
+// codes fit in kSkinnyFusedLds bytes of LDS (gemm_skinny.hip).  qa_out and
+// s_tok_out may be null; when given they receive the codes and scales.
+constexpr int64_t kSkinnyFusedMaxM = 16;
+constexpr int64_t kSkinnyFusedLds = 64 * 1024 + 16 * 16;
+bool gemm_skinny_fused_fits(int64_t M, int64_t K);
+hipError_t launch_gemm_skinny_fused(const float* x, int64_t ldx, const uint8_t* qw, int64_t ldw, const float* s_ch,
+                                    uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K, uint8_t* qa_out,
+                                    float* s_tok_out, hipStream_t stream);
+
 // LDS-tiled MFMA scaled GEMM for larger M (gemm_tiled.hip).
 hipError_t launch_gemm_tiled(const uint8_t* qa, int64_t lda, const float* s_tok, const uint8_t* qw,
                              int64_t ldw, const float* s_ch, uint16_t* y, int64_t ldy, int64_t M, int64_t N,

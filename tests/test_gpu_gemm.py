@@ -121,8 +121,15 @@ def test_strided_operands_and_output():
     assert np.all(yh[:, N:] == 0)
 
 
-@pytest.mark.parametrize("M,N,K", [(8, 512, 1024), (200, 300, 640)])
+# M <= 16 rows whose codes fit in LDS take the one-kernel path (rows up to
+# 4096 held in registers, longer rows read twice); the rest quantize first.
+FUSED_SHAPES = [(1, 16, 16), (8, 512, 1024), (5, 4096 + 48, 272), (16, 300, 4096), (12, 3000, 4112),
+                (8, 1000, 8192), (16, 100, 4112), (17, 300, 640), (200, 300, 640)]
+
+
+@pytest.mark.parametrize("M,N,K", FUSED_SHAPES)
 def test_fused_equals_quantize_then_gemm(M, N, K):
+    log(f"fused M={M} N={N} K={K}")
     x, qa, st, qw, sc = _quantized_problem(M, N, K, seed=11)
     xd, qwd, scd = to_dev(x), to_dev(qw), to_dev(sc)
     qa_out = torch.empty((M, K), dtype=torch.uint8, device=DEV)
@@ -135,6 +142,10 @@ def test_fused_equals_quantize_then_gemm(M, N, K):
     assert_scales_equal(to_host(st_out), st, "fused scales")
     assert np.array_equal(to_host(y_f), to_host(y_s))
     assert np.array_equal(to_host(y_f2), to_host(y_s))
+    st_only = torch.empty(M, dtype=torch.float32, device=DEV)
+    y_f3 = fp8.fp8_quant_gemm_fused(xd, qwd, scd, s_tok_out=st_only)
+    assert_scales_equal(to_host(st_only), st, "fused scales only")
+    assert np.array_equal(to_host(y_f3), to_host(y_s))
     ref, ab = oracle.gemm_ref(qa, st, qw, sc)
     assert_within_tolerance(to_host(y_f), ref, ab, "fused")
 

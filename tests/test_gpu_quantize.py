@@ -118,3 +118,57 @@ def test_device_cast_sweep_all_fp32_magnitudes_up_to_448():
             assert_codes_equal(got, want, f"sweep sign={sign >> 31} start=0x{start:08x}")
             start += n
         log(f"  sweep sign={sign >> 31} done ({total} patterns)")
+
+
+def _boundary_rows(n_rows, seed):
+    """Rows whose first element A sets the scale s = fl32(A / 448) (A spans
+    1e-9 .. 1e30 log-uniformly) and whose other elements lie within two ulps
+    of s times an E4M3 magnitude or a midpoint between two neighbouring
+    magnitudes -- the quotients x / s where an error of one ulp would change
+    the code.  Both signs; the rest of the row is zero."""
+    from tests._helpers import torch_e4m3_values
+    mags = np.unique(np.abs(torch_e4m3_values()[np.isfinite(torch_e4m3_values())])).astype(np.float64)
+    pts = np.concatenate([mags, 0.5 * (mags[1:] + mags[:-1])])
+    pts = pts[pts <= 440.0]
+    rng = np.random.default_rng(seed)
+    K = 16 * ((len(pts) * 5 * 2 + 1 + 15) // 16)
+    x = np.zeros((n_rows, K), np.float32)
+    for i in range(n_rows):
+        A = np.float32(10.0 ** rng.uniform(-9, 30))
+        s = np.float32(A) / np.float32(448.0)
+        vals = []
+        for p in pts:
+            x0 = np.float32(p * np.float64(s))
+            lo = x0
+            for _ in range(2):
+                lo = np.nextafter(lo, np.float32(0))
+            v = lo
+            for _ in range(5):
+                vals.append(v)
+                v = np.nextafter(v, np.float32(np.inf))
+        vals = np.array(vals, np.float32)
+        row = np.concatenate([[A], vals, -vals]).astype(np.float32)
+        x[i, :row.size] = row
+    return x
+
+
+def test_boundary_quotients_with_random_scales():
+    x = _boundary_rows(64, seed=5)
+    log(f"boundary rows {x.shape}")
+    _check(x, "boundary quotients")
+
+
+def test_fused_path_codes_on_boundary_quotients():
+    """The fused decode kernel quantizes in its own prologue: its codes and
+    scales (returned through qa_out / s_tok_out) must equal the oracle's."""
+    x = _boundary_rows(8, seed=6)[:, :4096]
+    M, K = x.shape
+    N = 64
+    qw = torch.full((N, K), 0x38, dtype=torch.uint8, device=DEV)
+    sc = torch.ones(N, dtype=torch.float32, device=DEV)
+    qa_out = torch.empty((M, K), dtype=torch.uint8, device=DEV)
+    st_out = torch.empty(M, dtype=torch.float32, device=DEV)
+    fp8.fp8_quant_gemm_fused(to_dev(x), qw, sc, qa_out=qa_out, s_tok_out=st_out)
+    oq, os_ = oracle.quantize_rows(x)
+    assert_scales_equal(to_host(st_out), os_, "fused boundary scales")
+    assert_codes_equal(to_host(qa_out), oq, "fused boundary codes")
