@@ -137,8 +137,9 @@ def fp8_quantize_per_token(x, q=None, scales=None, stream=None):
 def fp8_gemm_scaled(qa, s_tok, qw, s_ch, y=None, ws=None, stream=None):
     """y[m,n] = bf16(sum_k e4m3(qa[m,k]) e4m3(qw[n,k]) * s_tok[m] * s_ch[n]).
 
-    ws: optional uint8 workspace of fp8_workspace_bytes(M, N, K) bytes,
-    zero-filled before its first use (one such buffer can be reused)."""
+    ws: optional uint8 device workspace of at least fp8_workspace_bytes(M, N, K)
+    bytes (scratch: its contents on entry do not matter); allocated per call
+    when not given."""
     torch = _torch()
     M, K, lda = _rows(qa, torch.uint8, "qa")
     N, K2, ldw = _rows(qw, torch.uint8, "qw")
@@ -151,7 +152,7 @@ def fp8_gemm_scaled(qa, s_tok, qw, s_ch, y=None, ws=None, stream=None):
     _, _, ldy = _rows(y, torch.bfloat16, "y")
     if ws is None:
         need = int(lib().fp8_workspace_bytes(M, N, K))
-        ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=qa.device) if need > 0 else None
+        ws = torch.empty(need, dtype=torch.uint8, device=qa.device) if need > 0 else None
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check("fp8_gemm_scaled",
            lib().fp8_gemm_scaled(_ptr(qa), lda, _ptr(s_tok), _ptr(qw), ldw, _ptr(s_ch), _ptr(y), ldy, M, N, K,
@@ -177,7 +178,7 @@ def fp8_quant_gemm_fused(x, qw, s_ch, y=None, qa_out=None, s_tok_out=None, ws=No
         _vec(s_tok_out, torch.float32, "s_tok_out", M)
     need = fp8_workspace_bytes(M, N, K)
     if ws is None:
-        ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=x.device)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     ws_bytes = ws.numel() * ws.element_size()
     _check("fp8_quant_gemm_fused",
            lib().fp8_quant_gemm_fused(_ptr(x), ldx, _ptr(qw), ldw, _ptr(s_ch), _ptr(y), ldy, M, N, K,

@@ -73,8 +73,11 @@ fp8_status_t check_vector(const void* p, int64_t n) {
 
 fp8_status_t from_hip(hipError_t e) { return e == hipSuccess ? FP8_OK : FP8_ERR_DEVICE; }
 
-// Bytes the GEMM path itself needs for an M x N x K problem (none today).
-size_t gemm_ws_bytes(int64_t, int64_t, int64_t) { return 0; }
+// Bytes the GEMM path itself needs for an M x N x K problem: the skinny
+// kernel's fp32 split-k partial sums when it splits k, else none.
+size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K) {
+    return M <= fp8k::kSkinnyMaxM ? round_up(fp8k::gemm_skinny_ws_bytes(M, N, K), kAlign) : 0;
+}
 
 // Bytes the fused path stages its activation codes and scales in.
 size_t fused_stage_bytes(int64_t M, int64_t K) {
@@ -83,9 +86,9 @@ size_t fused_stage_bytes(int64_t M, int64_t K) {
 
 fp8_status_t gemm_dispatch(const uint8_t* qa, int64_t lda, const float* s_tok, const uint8_t* qw, int64_t ldw,
                            const float* s_ch, uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K,
-                           hipStream_t stream) {
+                           void* ws, hipStream_t stream) {
     if (M <= fp8k::kSkinnyMaxM)
-        return from_hip(fp8k::launch_gemm_skinny(qa, lda, s_tok, qw, ldw, s_ch, y, ldy, M, N, K, stream));
+        return from_hip(fp8k::launch_gemm_skinny(qa, lda, s_tok, qw, ldw, s_ch, y, ldy, M, N, K, ws, stream));
     if (K % 128 == 0)
         return from_hip(fp8k::launch_gemm_mfma(qa, lda, s_tok, qw, ldw, s_ch, y, ldy, M, N, K, stream));
     return from_hip(fp8k::launch_gemm_tiled(qa, lda, s_tok, qw, ldw, s_ch, y, ldy, M, N, K, stream));
@@ -142,8 +145,9 @@ fp8_status_t fp8_gemm_scaled(const uint8_t* qa, int64_t lda, const float* s_tok,
     const size_t need = gemm_ws_bytes(M, N, K);
     if (ws_bytes < need) return FP8_ERR_WORKSPACE;
     if (need > 0 && ws == nullptr) return FP8_ERR_INVALID_ARGUMENT;
+    if (need > 0 && !aligned16(ws)) return FP8_ERR_UNSUPPORTED;
     if (M == 0 || N == 0) return FP8_OK;
-    return gemm_dispatch(qa, lda, s_tok, qw, ldw, s_ch, y, ldy, M, N, K, stream);
+    return gemm_dispatch(qa, lda, s_tok, qw, ldw, s_ch, y, ldy, M, N, K, ws, stream);
 }
 
 fp8_status_t fp8_quant_gemm_fused(const float* x, int64_t ldx, const uint8_t* qw, int64_t ldw,
@@ -171,7 +175,7 @@ fp8_status_t fp8_quant_gemm_fused(const float* x, int64_t ldx, const uint8_t* qw
     float* s_tok = s_tok_out ? s_tok_out : reinterpret_cast<float*>(base + round_up((size_t)M * (size_t)K, kAlign));
     FP8_TRY(from_hip(fp8k::launch_quantize_rows(x, ldx, qa, K, s_tok, M, K, stream)));
     if (N == 0) return FP8_OK;
-    return gemm_dispatch(qa, K, s_tok, qw, ldw, s_ch, y, ldy, M, N, K, stream);
+    return gemm_dispatch(qa, K, s_tok, qw, ldw, s_ch, y, ldy, M, N, K, base + fused_stage_bytes(M, K), stream);
 }
 
 fp8_status_t fp8_gemm_grouped_scaled(const uint8_t* qa, const float* s_tok, const int32_t* row_token,

@@ -29,17 +29,23 @@ __device__ __forceinline__ void issue_order_fence() { __builtin_amdgcn_sched_bar
 
 // Lane `lane` supplies bytes [16g, 16g+16) and [64+16g, 64+16g+16) of a
 // 128-byte k chunk (g = lane / 16) for A and B alike.
+//
+// Split K (part != nullptr): workgroup (x, z) covers the k chunks
+// [z * split_chunks, (z + 1) * split_chunks) and writes its fp32 sums to
+// part[z][m][n] (row stride N); skinny_splitk_reduce adds the splits in order
+// z = 0, 1, ... and applies the epilogue.
 template <int MT, int NT, int KW, int DEPTH>
 __global__ __launch_bounds__(KW * 64) void gemm_skinny_kernel(
     const uint8_t* __restrict__ qa, int64_t lda, const float* __restrict__ s_tok,
     const uint8_t* __restrict__ qw, int64_t ldw, const float* __restrict__ s_ch,
-    uint16_t* __restrict__ y, int64_t ldy, int M, int N, int K) {
+    uint16_t* __restrict__ y, int64_t ldy, int M, int N, int K, float* __restrict__ part, int split_chunks) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int r16 = lane & 15;
     const int g = lane >> 4;
     const int n0 = blockIdx.x * (NT * 16);
-    const int nchunks = (K + 127) >> 7;
+    const int c0 = blockIdx.z * split_chunks;
+    const int nchunks = min((K + 127) >> 7, c0 + split_chunks) - c0;
     const int steps = nchunks > wave ? (nchunks - wave + KW - 1) / KW : 0;
 
     const uint8_t* wrow[NT];
@@ -74,7 +80,7 @@ __global__ __launch_bounds__(KW * 64) void gemm_skinny_kernel(
     // K read the row's first bytes (K >= 16 whenever a step runs).  Rows past
     // N or M read row 0: they only feed output elements that are never stored.
     auto load_step = [&](int s, v4i (&wd)[NT][2], v4i (&xd)[MT][2]) {
-        const int kb = (wave + KW * s) * 128;
+        const int kb = (c0 + wave + KW * s) * 128;
         const int o0 = kb + 16 * g < K ? kb + 16 * g : 0;
         const int o1 = kb + 64 + 16 * g < K ? kb + 64 + 16 * g : 0;
 #pragma unroll
@@ -99,7 +105,7 @@ __global__ __launch_bounds__(KW * 64) void gemm_skinny_kernel(
 #pragma unroll
             for (int d = 0; d < DEPTH; ++d) {
                 const int s = s0 + d;
-                const int kb = (wave + KW * s) * 128;
+                const int kb = (c0 + wave + KW * s) * 128;
                 const bool ok0 = s < steps && kb + 16 * g < K;
                 const bool ok1 = s < steps && kb + 64 + 16 * g < K;
                 v8i xf[MT];
@@ -133,6 +139,15 @@ __global__ __launch_bounds__(KW * 64) void gemm_skinny_kernel(
         const int m = 16 * i + r16;
         const int nb = n0 + 16 * j + 4 * g;
         if (m >= M || nb >= N) continue;
+        if (part != nullptr) {
+            float* pr = part + ((int64_t)blockIdx.z * M + m) * N;
+            if (nb + 3 < N && (N & 3) == 0) {
+                *reinterpret_cast<float4*>(pr + nb) = make_float4(sum[0], sum[1], sum[2], sum[3]);
+            } else {
+                for (int v = 0; v < 4 && nb + v < N; ++v) pr[nb + v] = sum[v];
+            }
+            continue;
+        }
         const float st = s_tok[m];
         uint16_t* yr = y + (int64_t)m * ldy;
         if (nb + 3 < N && (ldy & 3) == 0) {
@@ -321,51 +336,140 @@ __global__ __launch_bounds__(KW * 64) void gemm_skinny_fused_kernel(
     }
 }
 
+// y[m, n] = bf16_rne((part[0][m][n] + part[1][m][n] + ...) * (s_tok[m] * s_ch[n])),
+// the splits added in order; one thread per 4 consecutive outputs.
+__global__ __launch_bounds__(256) void skinny_splitk_reduce(const float* __restrict__ part, int splits, int M, int N,
+                                                           const float* __restrict__ s_tok,
+                                                           const float* __restrict__ s_ch, uint16_t* __restrict__ y,
+                                                           int64_t ldy) {
+    const int n4 = (N + 3) >> 2;
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= (int64_t)M * n4) return;
+    const int m = (int)(t / n4);
+    const int nb = (int)(t - (int64_t)m * n4) * 4;
+    const int64_t plane = (int64_t)M * N;
+    const float* p = part + (int64_t)m * N + nb;
+    const float st = s_tok[m];
+    uint16_t* yr = y + (int64_t)m * ldy;
+    if (nb + 3 < N && (N & 3) == 0 && (ldy & 3) == 0) {
+        float4 a = *reinterpret_cast<const float4*>(p);
+        for (int z = 1; z < splits; ++z) {
+            const float4 b = *reinterpret_cast<const float4*>(p + z * plane);
+            a.x += b.x;
+            a.y += b.y;
+            a.z += b.z;
+            a.w += b.w;
+        }
+        const float4 sc = *reinterpret_cast<const float4*>(s_ch + nb);
+        uint2 o;
+        o.x = pack_bf16x2(a.x * (st * sc.x), a.y * (st * sc.y));
+        o.y = pack_bf16x2(a.z * (st * sc.z), a.w * (st * sc.w));
+        *reinterpret_cast<uint2*>(yr + nb) = o;
+    } else {
+        for (int v = 0; v < 4 && nb + v < N; ++v) {
+            float a = p[v];
+            for (int z = 1; z < splits; ++z) a += p[z * plane + v];
+            yr[nb + v] = (uint16_t)bf16_rne_bits(a * (st * s_ch[nb + v]));
+        }
+    }
+}
+
 template <int MT, int NT, int KW>
 static void launch_cfg(dim3 grid, hipStream_t stream, const uint8_t* qa, int64_t lda, const float* s_tok,
                        const uint8_t* qw, int64_t ldw, const float* s_ch, uint16_t* y, int64_t ldy, int M, int N,
-                       int K) {
+                       int K, float* part, int split_chunks) {
     constexpr int DEPTH = (MT * NT <= 2) ? 4 : 2;
     hipLaunchKernelGGL((gemm_skinny_kernel<MT, NT, KW, DEPTH>), grid, dim3(KW * 64), 0, stream, qa, lda, s_tok, qw,
-                       ldw, s_ch, y, ldy, M, N, K);
+                       ldw, s_ch, y, ldy, M, N, K, part, split_chunks);
 }
 
 template <int MT>
 static void launch_mt(int nt, dim3 grid, hipStream_t stream, const uint8_t* qa, int64_t lda, const float* s_tok,
                       const uint8_t* qw, int64_t ldw, const float* s_ch, uint16_t* y, int64_t ldy, int M, int N,
-                      int K) {
+                      int K, float* part, int split_chunks) {
     switch (nt) {
-        case 8: launch_cfg<MT, 8, 4>(grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, ldy, M, N, K); break;
-        case 4: launch_cfg<MT, 4, 8>(grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, ldy, M, N, K); break;
-        case 2: launch_cfg<MT, 2, 8>(grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, ldy, M, N, K); break;
-        default: launch_cfg<MT, 1, 8>(grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, ldy, M, N, K); break;
+        case 8: launch_cfg<MT, 8, 4>(grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, ldy, M, N, K, part, split_chunks); break;
+        case 4: launch_cfg<MT, 4, 8>(grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, ldy, M, N, K, part, split_chunks); break;
+        case 2: launch_cfg<MT, 2, 8>(grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, ldy, M, N, K, part, split_chunks); break;
+        default: launch_cfg<MT, 1, 8>(grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, ldy, M, N, K, part, split_chunks); break;
     }
+}
+
+// Weight rows per workgroup (16 * nt) and the number of k splits.  The
+// activation fragments are re-read from L2 once per 16 * nt weight rows, so
+// larger nt means less L2 traffic; the grid should still hold about one
+// workgroup per CU (measured on MI355X: 256 workgroups of 4 waves, one per
+// CU, beat partial second rounds).  One activation tile (M <= 16): the largest
+// nt <= 4 that leaves >= 224 workgroups, never split (the one-kernel fused
+// path must produce the same bits).  More tiles: nt = 8 (4 waves) when that
+// leaves >= 224 workgroups; when it leaves at most 128, k is split into
+// floor(256 / workgroups) parts (each keeping at least two 128-byte chunks
+// per wave); in between, nt = 4 (8 waves).  Split workgroups write fp32
+// partial sums to the workspace, which a second kernel adds up in a fixed
+// order.
+SkinnyPlan skinny_plan(int64_t M, int64_t N, int64_t K) {
+    SkinnyPlan p{};
+    p.mt = (int)((M + 15) / 16);
+    p.splits = 1;
+    const int64_t chunks = (K + 127) / 128;
+    p.split_chunks = (int)chunks;
+    auto groups = [&](int nt) { return (N + 16 * nt - 1) / (16 * nt); };
+    auto spread = [&](int nt_max) {
+        for (int c = nt_max; c >= 1; c >>= 1)
+            if (groups(c) >= 224) return c;
+        return 1;
+    };
+    if (p.mt == 1) {
+        p.nt = spread(4);
+        return p;
+    }
+    const int64_t g8 = groups(8);
+    if (g8 >= 224) {
+        p.nt = 8;
+        return p;
+    }
+    if (g8 > 128) {
+        p.nt = 4;
+        return p;
+    }
+    int64_t splits = 256 / g8;
+    const int64_t max_splits = chunks / (2 * 4);
+    if (splits > max_splits) splits = max_splits;
+    if (splits > 16) splits = 16;
+    if (splits <= 1) {
+        p.nt = spread(8);
+        return p;
+    }
+    p.nt = 8;
+    p.split_chunks = (int)((chunks + splits - 1) / splits);
+    p.splits = (int)((chunks + p.split_chunks - 1) / p.split_chunks);
+    return p;
+}
+
+size_t gemm_skinny_ws_bytes(int64_t M, int64_t N, int64_t K) {
+    if (M <= 0 || N <= 0 || M > kSkinnyMaxM) return 0;
+    const SkinnyPlan p = skinny_plan(M, N, K);
+    return p.splits > 1 ? (size_t)p.splits * (size_t)M * (size_t)N * sizeof(float) : 0;
 }
 
 hipError_t launch_gemm_skinny(const uint8_t* qa, int64_t lda, const float* s_tok, const uint8_t* qw,
                               int64_t ldw, const float* s_ch, uint16_t* y, int64_t ldy, int64_t M, int64_t N,
-                              int64_t K, hipStream_t stream) {
+                              int64_t K, void* ws, hipStream_t stream) {
     if (M <= 0 || N <= 0) return hipSuccess;
-    const int mt = (int)((M + 15) / 16);
-    // Weight rows per workgroup (16 * NT): as many as still leave >= 224
-    // workgroups (the activation fragments are re-read from L2 once per
-    // 16 * NT weight rows, so larger NT means less L2 traffic), up to 8 tiles
-    // when M needs 3-4 activation tiles and 4 otherwise.  Waves per
-    // workgroup that split K: 8, or 4 with NT = 8 (register budget).
-    const int nt_max = mt >= 3 ? 8 : 4;
-    int nt = 1;
-    for (int c = nt_max; c >= 1; c >>= 1)
-        if ((N + 16 * c - 1) / (16 * c) >= 224) {
-            nt = c;
-            break;
-        }
-    const dim3 grid((unsigned)((N + 16 * nt - 1) / (16 * nt)));
+    const SkinnyPlan p = skinny_plan(M, N, K);
+    float* part = p.splits > 1 ? static_cast<float*>(ws) : nullptr;
+    const dim3 grid((unsigned)((N + 16 * p.nt - 1) / (16 * p.nt)), 1, (unsigned)p.splits);
     const int m = (int)M, n = (int)N, k = (int)K;
-    switch (mt) {
-        case 1: launch_mt<1>(nt, grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, ldy, m, n, k); break;
-        case 2: launch_mt<2>(nt, grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, ldy, m, n, k); break;
-        case 3: launch_mt<3>(nt, grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, ldy, m, n, k); break;
-        default: launch_mt<4>(nt, grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, ldy, m, n, k); break;
+    switch (p.mt) {
+        case 1: launch_mt<1>(p.nt, grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, ldy, m, n, k, part, p.split_chunks); break;
+        case 2: launch_mt<2>(p.nt, grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, ldy, m, n, k, part, p.split_chunks); break;
+        case 3: launch_mt<3>(p.nt, grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, ldy, m, n, k, part, p.split_chunks); break;
+        default: launch_mt<4>(p.nt, grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, ldy, m, n, k, part, p.split_chunks); break;
+    }
+    if (part != nullptr) {
+        const int64_t threads = M * ((N + 3) / 4);
+        hipLaunchKernelGGL(skinny_splitk_reduce, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, part,
+                           p.splits, m, n, s_tok, s_ch, y, ldy);
     }
     return hipGetLastError();
 }

@@ -15,10 +15,18 @@ hipError_t launch_quantize_rows(const float* x, int64_t ldx, uint8_t* q, int64_t
 // Largest M the skinny (decode) kernel takes.
 constexpr int64_t kSkinnyMaxM = 64;
 
-// Skinny-M scaled GEMM, M <= kSkinnyMaxM (gemm_skinny.hip).
+// Skinny-M scaled GEMM, M <= kSkinnyMaxM (gemm_skinny.hip).  Shapes with few
+// weight rows and long k split k across workgroups; they need
+// gemm_skinny_ws_bytes(M, N, K) bytes of workspace in ws (fp32 partial sums,
+// fully overwritten by every call, no zero fill needed).
+struct SkinnyPlan {
+    int mt, nt, splits, split_chunks;
+};
+SkinnyPlan skinny_plan(int64_t M, int64_t N, int64_t K);
+size_t gemm_skinny_ws_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_skinny(const uint8_t* qa, int64_t lda, const float* s_tok, const uint8_t* qw,
                               int64_t ldw, const float* s_ch, uint16_t* y, int64_t ldy, int64_t M, int64_t N,
-                              int64_t K, hipStream_t stream);
+                              int64_t K, void* ws, hipStream_t stream);
 
 // Quantize + skinny GEMM in one kernel, for M <= kSkinnyFusedMaxM rows whose
 // codes fit in kSkinnyFusedLds bytes of LDS (gemm_skinny.hip).  qa_out and

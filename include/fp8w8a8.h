@@ -46,8 +46,10 @@
  *   - An empty problem (M == 0, R == 0 or N == 0) is a no-op returning FP8_OK.
  *     K == 0 is valid for the GEMMs (y = 0) and for the quantizer (scales are
  *     the 1e-12 floor).
- *   - Inputs are assumed finite.  Calls that share a workspace must not run
- *     concurrently.
+ *   - Inputs are assumed finite (E4M3 operand codes 0x7F / 0xFF are NaN).
+ *   - ws is caller-owned device scratch, 16-byte aligned when it is needed;
+ *     its contents on entry do not matter and are undefined after the call.
+ *     Calls that share a workspace must not run concurrently.
  */
 #ifndef FP8W8A8_H
 #define FP8W8A8_H
@@ -88,7 +90,10 @@ fp8_status_t fp8_quantize_per_token(const float* x, int64_t rows, int64_t K, int
  *   y[m,n] = bf16_rne( (sum_k e4m3(qa[m,k]) * e4m3(qw[n,k])) * (s_tok[m] * s_ch[n]) )
  * Skinny M (decode, M <= 64) streams W once from HBM; larger M runs the
  * LDS-tiled MFMA kernel.  ws: device scratch of at least
- * fp8_workspace_bytes(M, N, K) bytes (may be NULL when that is 0).
+ * fp8_workspace_bytes(M, N, K) bytes (may be NULL when that is 0).  Skinny
+ * shapes with more than 16 rows, few weight rows and long K split K across
+ * workgroups and keep fp32 partial sums there (added in a fixed order, so
+ * results are reproducible).
  */
 fp8_status_t fp8_gemm_scaled(const uint8_t* qa, int64_t lda, const float* s_tok,
                              const uint8_t* qw, int64_t ldw, const float* s_ch,
@@ -102,6 +107,10 @@ fp8_status_t fp8_gemm_scaled(const uint8_t* qa, int64_t lda, const float* s_tok,
  * qa_out [M, K] (stride K) and s_tok_out [M] are optional (NULL allowed);
  * when given they receive the activation codes and scales.  ws must hold at
  * least fp8_workspace_bytes(M, N, K) bytes.
+ * For M <= 16 rows with M * (K + 16) <= 65792 and ceil(K / 256) <= 16
+ * (M <= 8) or <= 8 (M <= 16), and N > 0, the call runs as one kernel that
+ * quantizes x in each workgroup's prologue (ws is then not touched); the
+ * codes, scales and y are the same bytes either way.
  */
 fp8_status_t fp8_quant_gemm_fused(const float* x, int64_t ldx, const uint8_t* qw, int64_t ldw,
                                   const float* s_ch, uint16_t* y, int64_t ldy,

@@ -34,8 +34,11 @@ def _gemm(qa, st, qw, sc):
 
 
 # M <= 64 runs the skinny kernel, larger M the tiled one; shapes span several
-# tiles with ragged M, N and K tails.
+# tiles with ragged M, N and K tails.  (64, 1024, 4096), (40, 1000, 8240) and
+# (17, 300, 16384) have few weight rows and long K: the skinny kernel splits
+# K there (4, 8 and 16 parts; the 8240 one ends in a partial 128-byte chunk).
 SHAPES = [(1, 16, 16), (8, 200, 160), (16, 4096 + 48, 512), (33, 300, 1040), (64, 520, 2064),
+          (64, 1024, 4096), (40, 1000, 8240), (17, 300, 16384),
           (65, 272, 384), (200, 700, 1168), (513, 257, 2064), (300, 1024, 4096),
           (129, 1000, 640), (777, 264, 1280), (256, 256, 128)]
 
@@ -121,6 +124,27 @@ def test_strided_operands_and_output():
     assert np.all(yh[:, N:] == 0)
 
 
+def test_split_k_strided_output_and_stale_workspace():
+    """A split-K shape with strided operands and output, through a workspace
+    that holds garbage on entry (its contents must not matter)."""
+    M, N, K = 48, 1000, 8192 + 16
+    _, qa, st, qw, sc = _quantized_problem(M, N, K, seed=9)
+    A = torch.zeros((M, K + 48), dtype=torch.uint8, device=DEV)
+    A[:, :K] = to_dev(qa)
+    W = torch.zeros((N, K + 16), dtype=torch.uint8, device=DEV)
+    W[:, :K] = to_dev(qw)
+    Y = torch.zeros((M, N + 3), dtype=torch.bfloat16, device=DEV)
+    need = fp8.fp8_workspace_bytes(M, N, K)
+    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device=DEV)
+    fp8.fp8_gemm_scaled(A[:, :K], to_dev(st), W[:, :K], to_dev(sc), y=Y[:, :N], ws=ws)
+    yh = to_host(Y)
+    ref, ab = oracle.gemm_ref(qa, st, qw, sc)
+    assert_within_tolerance(yh[:, :N], ref, ab, "split-k strided")
+    assert np.all(yh[:, N:] == 0)
+    y2 = to_host(fp8.fp8_gemm_scaled(to_dev(qa), to_dev(st), to_dev(qw), to_dev(sc)))
+    assert np.array_equal(y2, yh[:, :N])
+
+
 # M <= 16 rows whose codes fit in LDS take the one-kernel path (rows up to
 # 4096 held in registers, longer rows read twice); the rest quantize first.
 FUSED_SHAPES = [(1, 16, 16), (8, 512, 1024), (5, 4096 + 48, 272), (16, 300, 4096), (12, 3000, 4112),
@@ -151,7 +175,7 @@ def test_fused_equals_quantize_then_gemm(M, N, K):
 
 
 def test_repeatable_bits():
-    for (M, N, K) in [(64, 4096, 2048), (512, 512, 1024)]:
+    for (M, N, K) in [(64, 4096, 2048), (64, 1024, 8192), (512, 512, 1024)]:
         _, qa, st, qw, sc = _quantized_problem(M, N, K, seed=3)
         a, b, c, d = to_dev(qa), to_dev(st), to_dev(qw), to_dev(sc)
         y1 = to_host(fp8.fp8_gemm_scaled(a, b, c, d))
