@@ -22,9 +22,11 @@
 //   second half as soon as its last first-half MFMA has issued;
 //   wait (vmcnt) for this wave's DMA of stage s+1 and (lgkmcnt) for its reads
 //   of stage s; barrier: stage s+1 is complete in LDS and nobody reads stage
-//   s any more -> issue the DMA of stage s+2 into stage s's buffer;
-//   second-half MFMAs of stage s, refilling the registers with the first
-//   half of stage s+1.
+//   s any more -> the DMA of stage s+2 may go into stage s's buffer;
+//   second-half MFMAs of stage s, each followed by one DMA instruction of
+//   stage s+2, refilling the registers with the first half of stage s+1.
+// Scheduling hints alternate MFMAs and LDS reads within each half (measured
+// on MI355X: about 8% faster than letting them bunch).
 // One barrier per 32 MFMAs, LDS reads overlapped with MFMAs, a whole step of
 // MFMA time to hide each stage's load.  The compiler does not track
 // DMA-written LDS, so the waits are explicit and compiler memory fences keep
@@ -91,6 +93,17 @@ __device__ __forceinline__ v8i read_frag(const uint8_t* tile, int row, int h, in
     const v4i lo = *reinterpret_cast<const v4i*>(tile + row * kBK + (((4 * h + g) ^ s) << 4));
     const v4i hi = *reinterpret_cast<const v4i*>(tile + row * kBK + (((4 * h + 2 + g) ^ s) << 4));
     return join(lo, hi);
+}
+
+// Scheduling hint for a half step (16 MFMAs and the 16 LDS reads that refill
+// the fragments): alternate them, so the reads spread over the MFMA time
+// instead of bunching after it.
+__device__ __forceinline__ void interleave_mfma_reads() {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+    }
 }
 
 }  // namespace
@@ -275,6 +288,19 @@ __global__ __launch_bounds__(kThreadsM, 1) void gemm_mfma_kernel(MfmaArgs p) {
     }
     const int nlast = p.N - 1;
 
+    // DMA instruction j (0 .. PER_STAGE - 1) of stage kt into ring slot `slot`.
+    auto issue_one = [&](int kt, int slot, int j) {
+        uint8_t* base = smem + slot * STAGE;
+        const int koff = kt * kBK;
+        if (j < DA) {
+            const int row = (wave * DA + j) * 8 + lrow;
+            const int n = min(n0 + row, nlast);  // rows past N feed discarded columns
+            dma16(qw + (int64_t)n * ldw + koff + ((lpos ^ dswz(row)) << 4), base + (wave * DA + j) * 1024);
+        } else {
+            const int jb = j - DA;
+            dma16(bsrc[jb] + koff, base + BN * kBK + (wave * DB + jb) * 1024);
+        }
+    };
     // Stage kt goes to ring slot `slot` (0 or 1).
     auto issue_stage = [&](int kt, int slot) {
         uint8_t* base = smem + slot * STAGE;
@@ -318,7 +344,41 @@ __global__ __launch_bounds__(kThreadsM, 1) void gemm_mfma_kernel(MfmaArgs p) {
 #pragma unroll
         for (int a = 0; a < FN; ++a) fa[a] = read_a(0, 0, a);
     }
-    for (int s = 0; s < KT; ++s) {
+    // Steps with a stage s+2 to load: no branches in the body, the DMA
+    // instructions of stage s+2 issued one per second-half MFMA (in program
+    // order they must precede the LDS reads that follow them, which keeps them
+    // spread out instead of in one burst after the barrier).
+    static_assert(PER_STAGE <= FN * FM, "one DMA instruction per second-half MFMA");
+    int s = 0;
+    for (; s + 2 < KT; ++s) {
+        const int cur = s & 1;
+#pragma unroll
+        for (int a = 0; a < FN; ++a) {
+#pragma unroll
+            for (int b = 0; b < FM; ++b) {
+                acc[a][b] = mfma_32x32x64_e4m3(fa[a], fb[b], acc[a][b]);
+                if (a == FN - 1) fb[b] = read_b(cur, 1, b);
+            }
+            fa[a] = read_a(cur, 1, a);
+        }
+        interleave_mfma_reads();
+        wait_dma<PER_STAGE>(0);  // this wave's part of stage s+1 landed
+        wait_lds_reads();        // ... and its reads of stage s are done
+        block_barrier();
+#pragma unroll
+        for (int a = 0; a < FN; ++a) {
+#pragma unroll
+            for (int b = 0; b < FM; ++b) {
+                acc[a][b] = mfma_32x32x64_e4m3(fa[a], fb[b], acc[a][b]);
+                if (a * FM + b < PER_STAGE) issue_one(s + 2, cur, a * FM + b);
+                if (a == FN - 1) fb[b] = read_b(cur ^ 1, 0, b);
+            }
+            fa[a] = read_a(cur ^ 1, 0, a);
+        }
+        interleave_mfma_reads();
+    }
+    // The last two steps (nothing left to load).
+    for (; s < KT; ++s) {
         const int cur = s & 1;
         const bool more = s + 1 < KT;
         // first K half of stage s; refill with the second half
@@ -331,11 +391,11 @@ __global__ __launch_bounds__(kThreadsM, 1) void gemm_mfma_kernel(MfmaArgs p) {
             }
             fa[a] = read_a(cur, 1, a);
         }
+        interleave_mfma_reads();
         if (more) {
-            wait_dma<PER_STAGE>(0);  // this wave's part of stage s+1 landed
-            wait_lds_reads();        // ... and its reads of stage s are done
+            wait_dma<PER_STAGE>(0);
+            wait_lds_reads();
             block_barrier();
-            if (s + 2 < KT) issue_stage(s + 2, cur);
         }
         // second K half of stage s; refill with the first half of stage s+1
         // (the last step re-reads its own slot, unused)
@@ -349,6 +409,7 @@ __global__ __launch_bounds__(kThreadsM, 1) void gemm_mfma_kernel(MfmaArgs p) {
             }
             fa[a] = read_a(nxt, 0, a);
         }
+        interleave_mfma_reads();
     }
 
     // ---- epilogue: y = bf16_rne(acc * (s_tok * s_ch)) ----------------------
