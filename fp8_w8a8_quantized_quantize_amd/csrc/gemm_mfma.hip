@@ -4,9 +4,12 @@
 // §2.4; FP8 x FP8 with FP32 accumulation, precision/hardware page §2.3).
 //
 // Tile: BN weight rows (MFMA A operand) x BM activation rows (MFMA B operand),
-// 128 bytes of K per stage, two stages in LDS.  Four waves in a 2 x 2 grid,
-// each owning (BN/2) x (BM/2) outputs as 32x32x64 FP8 MFMA tiles (16
-// accumulators per lane); a stage is consumed as two 64-wide K halves.
+// 128 bytes of K per stage, two stages in LDS.  WN x WM waves, each owning
+// (BN/WN) x (BM/WM) outputs as 32x32x64 FP8 MFMA tiles (16 accumulators per
+// lane per tile); a stage is consumed as two 64-wide K halves.  The launchers
+// use 2 x 2 waves of 128 x 128: measured on MI355X, 2 x 4 waves (two per SIMD,
+// which doubles the LDS read rate a CU reaches) lose more to the 50% larger
+// LDS read volume of 128 x 64 wave tiles and to register spills.
 //
 // Data movement: global_load_lds_dwordx4 writes a stage straight into LDS
 // (no VGPR staging, no ds_write).  One DMA instruction covers 8 rows x 128
@@ -45,7 +48,6 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 namespace {
 
 constexpr int kBK = 128;      // K bytes per stage
-constexpr int kThreadsM = 256;
 
 __device__ __forceinline__ v16f mfma_32x32x64_e4m3(const v8i& a, const v8i& b, const v16f& c) {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
@@ -95,14 +97,21 @@ __device__ __forceinline__ v8i read_frag(const uint8_t* tile, int row, int h, in
     return join(lo, hi);
 }
 
-// Scheduling hint for a half step (16 MFMAs and the 16 LDS reads that refill
-// the fragments): alternate them, so the reads spread over the MFMA time
-// instead of bunching after it.
+// Scheduling hint for a half step (MF MFMAs and the RD LDS reads that refill
+// the fragments): spread the reads evenly between the MFMAs instead of letting
+// them bunch after them.
+template <int MF, int RD>
 __device__ __forceinline__ void interleave_mfma_reads() {
+    constexpr int base = RD / MF, extra = RD % MF;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+    for (int i = 0; i < extra; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, base + 1, 0);  // LDS reads
+    }
+#pragma unroll
+    for (int i = extra; i < MF; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if constexpr (base > 0) __builtin_amdgcn_sched_group_barrier(0x100, base, 0);
     }
 }
 
@@ -184,22 +193,24 @@ __device__ void find_expert_tile(const MfmaArgs& p, int b, int* sh) {
     __syncthreads();
 }
 
-template <int BN, int BM, int STAGES, int GROUP_M, bool GROUPED>
-__global__ __launch_bounds__(kThreadsM, 1) void gemm_mfma_kernel(MfmaArgs p) {
-    constexpr int FN = BN / 64;                 // 32-row weight fragments per wave
-    constexpr int FM = BM / 64;                 // 32-row activation fragments per wave
-    constexpr int DA = BN / 32;                 // DMA instructions per wave per stage, weights
-    constexpr int DB = BM / 32;                 // ... activations
+template <int BN, int BM, int WN, int WM, int GROUP_M, bool GROUPED>
+__global__ __launch_bounds__(64 * WN * WM, 1) void gemm_mfma_kernel(MfmaArgs p) {
+    constexpr int NW = WN * WM;                 // waves: WN along the weight rows, WM along the activations
+    constexpr int NTH = 64 * NW;
+    constexpr int FN = BN / (32 * WN);          // 32-row weight fragments per wave
+    constexpr int FM = BM / (32 * WM);          // 32-row activation fragments per wave
+    constexpr int DA = BN / (8 * NW);           // DMA instructions per wave per stage, weights
+    constexpr int DB = BM / (8 * NW);           // ... activations
     constexpr int PER_STAGE = DA + DB;
     constexpr int STAGE = (BN + BM) * kBK;
-    static_assert(STAGES == 2, "two-stage ring");
+    static_assert(DA * 8 * NW == BN && DB * 8 * NW == BM, "whole DMA instructions per wave");
     static_assert(BM * BN * 2 <= 2 * STAGE, "the BF16 output tile must fit in the ring");
     int* sh = reinterpret_cast<int*>(smem + 2 * STAGE + 4 * (BN + BM));  // grouped tile lookup
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wn = wave & 1, wm = wave >> 1;
+    const int wn = wave % WN, wm = wave / WN;
     const int r32 = lane & 31, g = lane >> 5;
 
     // ---- output tile ------------------------------------------------------
@@ -260,8 +271,8 @@ __global__ __launch_bounds__(kThreadsM, 1) void gemm_mfma_kernel(MfmaArgs p) {
     constexpr int RING = 2 * STAGE;
     float* s_ch_t = reinterpret_cast<float*>(smem + RING);
     float* s_tok_t = s_ch_t + BN;
-    for (int i = tid; i < BN; i += kThreadsM) s_ch_t[i] = s_ch[min(n0 + i, p.N - 1)];
-    for (int i = tid; i < BM; i += kThreadsM) {
+    for (int i = tid; i < BN; i += NTH) s_ch_t[i] = s_ch[min(n0 + i, p.N - 1)];
+    for (int i = tid; i < BM; i += NTH) {
         const int ml = min(i, rows_valid - 1);
         if constexpr (GROUPED)
             s_tok_t[i] = p.s_tok[p.row_token[row_begin + m0 + ml]];
@@ -324,8 +335,8 @@ __global__ __launch_bounds__(kThreadsM, 1) void gemm_mfma_kernel(MfmaArgs p) {
             for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
 
     const int KT = p.K / kBK;
-    const int arow0 = wn * (BN / 2) + r32;
-    const int brow0 = wm * (BM / 2) + r32;
+    const int arow0 = wn * (BN / WN) + r32;
+    const int brow0 = wm * (BM / WM) + r32;
     auto read_a = [&](int slot, int h, int a) { return read_frag(smem + slot * STAGE, arow0 + a * 32, h, g); };
     auto read_b = [&](int slot, int h, int b) {
         return read_frag(smem + slot * STAGE + BN * kBK, brow0 + b * 32, h, g);
@@ -361,7 +372,7 @@ __global__ __launch_bounds__(kThreadsM, 1) void gemm_mfma_kernel(MfmaArgs p) {
             }
             fa[a] = read_a(cur, 1, a);
         }
-        interleave_mfma_reads();
+        interleave_mfma_reads<FN * FM, 2 * (FN + FM)>();
         wait_dma<PER_STAGE>(0);  // this wave's part of stage s+1 landed
         wait_lds_reads();        // ... and its reads of stage s are done
         block_barrier();
@@ -375,7 +386,7 @@ __global__ __launch_bounds__(kThreadsM, 1) void gemm_mfma_kernel(MfmaArgs p) {
             }
             fa[a] = read_a(cur ^ 1, 0, a);
         }
-        interleave_mfma_reads();
+        interleave_mfma_reads<FN * FM, 2 * (FN + FM)>();
     }
     // The last two steps (nothing left to load).
     for (; s < KT; ++s) {
@@ -391,7 +402,7 @@ __global__ __launch_bounds__(kThreadsM, 1) void gemm_mfma_kernel(MfmaArgs p) {
             }
             fa[a] = read_a(cur, 1, a);
         }
-        interleave_mfma_reads();
+        interleave_mfma_reads<FN * FM, 2 * (FN + FM)>();
         if (more) {
             wait_dma<PER_STAGE>(0);
             wait_lds_reads();
@@ -409,7 +420,7 @@ __global__ __launch_bounds__(kThreadsM, 1) void gemm_mfma_kernel(MfmaArgs p) {
             }
             fa[a] = read_a(nxt, 0, a);
         }
-        interleave_mfma_reads();
+        interleave_mfma_reads<FN * FM, 2 * (FN + FM)>();
     }
 
     // ---- epilogue: y = bf16_rne(acc * (s_tok * s_ch)) ----------------------
@@ -424,13 +435,13 @@ __global__ __launch_bounds__(kThreadsM, 1) void gemm_mfma_kernel(MfmaArgs p) {
     constexpr int CH = BN / 8;  // 16-byte chunks per tile row
 #pragma unroll
     for (int b = 0; b < FM; ++b) {
-        const int ml = wm * (BM / 2) + b * 32 + r32;
+        const int ml = wm * (BM / WM) + b * 32 + r32;
         const float st = s_tok_t[ml];
 #pragma unroll
         for (int a = 0; a < FN; ++a) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int nl = wn * (BN / 2) + a * 32 + 8 * q + 4 * g;
+                const int nl = wn * (BN / WN) + a * 32 + 8 * q + 4 * g;
                 const float4 sc4 = *reinterpret_cast<const float4*>(s_ch_t + nl);
                 const float sc[4] = {sc4.x, sc4.y, sc4.z, sc4.w};
                 uint2 o;
@@ -445,7 +456,7 @@ __global__ __launch_bounds__(kThreadsM, 1) void gemm_mfma_kernel(MfmaArgs p) {
     const bool vec_store = GROUPED ? (p.N & 7) == 0 : (p.ldy & 7) == 0;
     const int64_t ldy = GROUPED ? (int64_t)p.N : p.ldy;
 #pragma unroll 4
-    for (int id = tid; id < BM * CH; id += kThreadsM) {
+    for (int id = tid; id < BM * CH; id += NTH) {
         const int row = id / CH, c = id % CH;
         if (row >= rows_valid) continue;
         const int n = n0 + c * 8;
@@ -468,17 +479,17 @@ hipError_t launch_gemm_mfma(const uint8_t* qa, int64_t lda, const float* s_tok, 
                             const float* s_ch, uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K,
                             hipStream_t stream) {
     if (M <= 0 || N <= 0) return hipSuccess;
-    constexpr int BN = 256, BM = 256, ST = 2;
-    constexpr int LDS = ST * (BN + BM) * kBK + 4 * (BN + BM);  // ring + tile scales
+    constexpr int BN = 256, BM = 256, WN = 2, WM = 2;
+    constexpr int LDS = 2 * (BN + BM) * kBK + 4 * (BN + BM);  // ring + tile scales
     MfmaArgs p{};
     p.qa = qa; p.lda = lda; p.s_tok = s_tok; p.qw = qw; p.ldw = ldw; p.s_ch = s_ch; p.y = y; p.ldy = ldy;
     p.M = (int)M; p.N = (int)N; p.K = (int)K;
     p.tiles_m = (int)((M + BM - 1) / BM);
     p.tiles_n = (int)((N + BN - 1) / BN);
-    hipError_t e = FP8K_SET_LDS((gemm_mfma_kernel<BN, BM, ST, 4, false>), LDS);
+    hipError_t e = FP8K_SET_LDS((gemm_mfma_kernel<BN, BM, WN, WM, 4, false>), LDS);
     if (e != hipSuccess) return e;
     const unsigned grid = (unsigned)p.tiles_m * (unsigned)p.tiles_n;
-    hipLaunchKernelGGL((gemm_mfma_kernel<BN, BM, ST, 4, false>), dim3(grid), dim3(kThreadsM), LDS, stream, p);
+    hipLaunchKernelGGL((gemm_mfma_kernel<BN, BM, WN, WM, 4, false>), dim3(grid), dim3(64 * WN * WM), LDS, stream, p);
     return hipGetLastError();
 }
 
@@ -487,21 +498,22 @@ hipError_t launch_gemm_grouped_mfma(const uint8_t* qa, const float* s_tok, const
                                     int64_t T, int64_t R, int64_t E, int64_t N, int64_t K, hipStream_t stream) {
     (void)T;
     if (R <= 0 || N <= 0 || E <= 0) return hipSuccess;
-    constexpr int BN = 256, BM = 256, ST = 2;
-    constexpr int LDS = ST * (BN + BM) * kBK + 4 * (BN + BM) + 16;  // ring + tile scales + tile lookup
+    constexpr int BN = 256, BM = 256, WN = 2, WM = 2;
+    constexpr int LDS = 2 * (BN + BM) * kBK + 4 * (BN + BM) + 16;  // ring + tile scales + tile lookup
     MfmaArgs p{};
     p.qa = qa; p.lda = K; p.s_tok = s_tok; p.qw = qw; p.ldw = K; p.s_ch = s_ch; p.y = y; p.ldy = N;
     p.M = (int)R; p.N = (int)N; p.K = (int)K;
     p.tiles_n = (int)((N + BN - 1) / BN);
     p.row_token = row_token; p.offsets = offsets; p.E = (int)E;
     constexpr int GM = 4;
-    hipError_t e = FP8K_SET_LDS((gemm_mfma_kernel<BN, BM, ST, GM, true>), LDS);
+    hipError_t e = FP8K_SET_LDS((gemm_mfma_kernel<BN, BM, WN, WM, GM, true>), LDS);
     if (e != hipSuccess) return e;
     // sum over experts of ceil(rows_e / BM) <= ceil(R / BM) + E; each of the 8
     // XCD ranges holds at most ceil(total / 8) tiles
     const int64_t tiles_max = ((R + BM - 1) / BM + E) * p.tiles_n;
     const int64_t grid = 8 * ((tiles_max + 7) / 8);
-    hipLaunchKernelGGL((gemm_mfma_kernel<BN, BM, ST, GM, true>), dim3((unsigned)grid), dim3(kThreadsM), LDS, stream, p);
+    hipLaunchKernelGGL((gemm_mfma_kernel<BN, BM, WN, WM, GM, true>), dim3((unsigned)grid), dim3(64 * WN * WM), LDS, stream,
+                       p);
     return hipGetLastError();
 }
 
