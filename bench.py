@@ -56,6 +56,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches instead of one HIP-graph replay of the steps")
+    ap.add_argument("--out", choices=("bf16", "fp8"), default="bf16",
+                    help="bf16: the fused quantize+GEMM step (default); fp8: the FP8-output GEMM "
+                         "(fp8_gemm_scaled_fp8out on FP8 activations, dense workloads)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run 5 plain device copies of 512 MiB (reference for rocprofv3 FETCH/WRITE_SIZE)")
     ap.add_argument("--profile", action="store_true",
@@ -202,6 +205,11 @@ def main():
     log = lambda *a: print(*a, file=sys.stderr, flush=True)
     graph = not args.no_graph
 
+    if args.out == "fp8":
+        if w["kind"] != "dense":
+            print("--out fp8 is for the dense workloads", file=sys.stderr)
+            sys.exit(2)
+        return bench_fp8out(args, w, dev, steps, warmup, graph, log)
     if w["kind"] == "dense":
         M, N, K = w["M"], w["N"], w["K"]
         log(f"[bench] {args.workload}: generating inputs M={M} N={N} K={K}")
@@ -357,6 +365,57 @@ def main():
         "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp8e4m3 (fp32 accumulate, bf16 out)", "data": "synthetic (seeded; no dataset, no trained weights)",
         "config": cfg, "roofline": roof, "cpu_baseline": cpu, "detail": extra,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def bench_fp8out(args, w, dev, steps, warmup, graph, log):
+    """One step = fp8_gemm_scaled_fp8out: FP8 activation codes and scales in
+    (as a previous FP8-output layer leaves them), FP32 accumulation, the output
+    re-quantized per token to E4M3 codes and scales."""
+    import torch
+    import fp8_w8a8_quantized_quantize_amd as fp8
+    M, N, K = w["M"], w["N"], w["K"]
+    log(f"[bench] {args.workload} (FP8 output): generating inputs M={M} N={N} K={K}")
+    x, wt = gen_dense(w, args.seed)
+    wq, sc = fp8.fp8_quantize_per_token(torch.from_numpy(wt).to(dev))
+    copies = max(1, math.ceil(ROTATE_BYTES / (N * K)))
+    wcopies = [wq] + [wq.clone() for _ in range(copies - 1)]
+    qa, st = fp8.fp8_quantize_per_token(torch.from_numpy(x).to(dev))
+    q_out = torch.empty((M, N), dtype=torch.uint8, device=dev)
+    s_out = torch.empty(M, dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, fp8.fp8_fp8out_workspace_bytes(M, N, K)), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        fp8.fp8_gemm_scaled_fp8out(qa, st, wcopies[i % copies], sc, q_out=q_out, s_out=s_out, ws=ws)
+
+    total_ms, per = time_loop(step, steps, warmup, graph)
+    ms = total_ms / steps
+    flops = 2.0 * M * N * K
+    step_bytes = M * K + 4 * M + N * K + 4 * N + M * N + 4 * M   # codes+scales in, W, s_ch, codes+scales out
+    decode = M <= 64
+    if decode:
+        value, unit = step_bytes / (ms * 1e-3) / 1e9, "GB/s"
+        roof = dict(bound="hbm", achieved=round(value, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(value / HBM_PEAK_GBS, 4))
+        per_launch = f"{step_bytes} algorithmic bytes"
+    else:
+        value, unit = flops / (ms * 1e-3) / 1e12, "TFLOP/s"
+        roof = dict(bound="mfma", achieved=round(value, 1), peak=FP8_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=round(value / FP8_PEAK_TFLOPS, 4))
+        per_launch = f"{flops:.6g} FLOP"
+    roof.update(kernel="fp8_gemm_scaled_fp8out (GEMM with fp32 output, then the per-token output quantizer)",
+                per_launch=per_launch, avg_launch_us=round(ms * 1e3, 3), traffic=None)
+    cfg = dict(workload=args.workload, M=M, N=N, K=K, seed=args.seed, weight_copies=copies,
+               step="fp8_gemm_scaled_fp8out", out="e4m3 codes + fp32 per-token scales")
+    extra = dict(timing="hip-graph replay of the steps" if graph else "eager launches", step_us=round(ms * 1e3, 3))
+    if per:
+        extra.update(step_us_median=round(pct(per, 0.5) * 1e3, 3))
+    out = {
+        "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8e4m3 (fp32 accumulate, e4m3 out)", "data": "synthetic (seeded; no dataset, no trained weights)",
+        "config": cfg, "roofline": roof, "cpu_baseline": None, "detail": extra,
     }
     print(json.dumps(out), flush=True)
 

@@ -10,8 +10,9 @@ Entry points (same names as the C ABI):
   fp8_quantize_per_token(x)                -> (q uint8 [M,K], scales fp32 [M])
   fp8_gemm_scaled(qa, s_tok, qw, s_ch)     -> y bf16 [M,N]
   fp8_quant_gemm_fused(x, qw, s_ch)        -> y bf16 [M,N]  (optionally qa, s_tok)
+  fp8_gemm_scaled_fp8out(qa, s_tok, qw, s_ch) -> (q_out uint8 [M,N], s_out fp32 [M])  (optionally y32)
   fp8_gemm_grouped_scaled(qa, s_tok, row_token, expert_offsets, qw, s_ch) -> y bf16 [R,N]
-  fp8_workspace_bytes(M, N, K), fp8_grouped_workspace_bytes(T, R, E, N, K)
+  fp8_workspace_bytes(M, N, K), fp8_fp8out_workspace_bytes(M, N, K), fp8_grouped_workspace_bytes(T, R, E, N, K)
   fp8_status_string(code)
 """
 import ctypes
@@ -27,8 +28,9 @@ FP8_ERR_WORKSPACE = 3
 FP8_ERR_DEVICE = 4
 
 # exported symbols, as declared in include/fp8w8a8.h
-EXPORTS = ("fp8_quantize_per_token", "fp8_gemm_scaled", "fp8_quant_gemm_fused", "fp8_gemm_grouped_scaled",
-           "fp8_workspace_bytes", "fp8_grouped_workspace_bytes", "fp8_status_string")
+EXPORTS = ("fp8_quantize_per_token", "fp8_gemm_scaled", "fp8_quant_gemm_fused", "fp8_gemm_scaled_fp8out",
+           "fp8_gemm_grouped_scaled", "fp8_workspace_bytes", "fp8_fp8out_workspace_bytes",
+           "fp8_grouped_workspace_bytes", "fp8_status_string")
 
 _lib = None
 
@@ -54,6 +56,10 @@ def lib():
         L.fp8_gemm_scaled.argtypes = [vp, i64, vp, vp, i64, vp, vp, i64, i64, i64, i64, vp, sz, vp]
         L.fp8_quant_gemm_fused.restype = st
         L.fp8_quant_gemm_fused.argtypes = [vp, i64, vp, i64, vp, vp, i64, i64, i64, i64, vp, vp, vp, sz, vp]
+        L.fp8_gemm_scaled_fp8out.restype = st
+        L.fp8_gemm_scaled_fp8out.argtypes = [vp, i64, vp, vp, i64, vp, vp, i64, vp, vp, i64, i64, i64, vp, sz, vp]
+        L.fp8_fp8out_workspace_bytes.restype = sz
+        L.fp8_fp8out_workspace_bytes.argtypes = [i64, i64, i64]
         L.fp8_gemm_grouped_scaled.restype = st
         L.fp8_gemm_grouped_scaled.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, sz, vp]
         L.fp8_workspace_bytes.restype = sz
@@ -109,6 +115,10 @@ def _vec(t, dtype, name, n):
 
 def fp8_workspace_bytes(M, N, K):
     return int(lib().fp8_workspace_bytes(M, N, K))
+
+
+def fp8_fp8out_workspace_bytes(M, N, K):
+    return int(lib().fp8_fp8out_workspace_bytes(M, N, K))
 
 
 def fp8_grouped_workspace_bytes(T, R, E, N, K):
@@ -184,6 +194,35 @@ def fp8_quant_gemm_fused(x, qw, s_ch, y=None, qa_out=None, s_tok_out=None, ws=No
            lib().fp8_quant_gemm_fused(_ptr(x), ldx, _ptr(qw), ldw, _ptr(s_ch), _ptr(y), ldy, M, N, K,
                                       _ptr(qa_out), _ptr(s_tok_out), _ptr(ws), ws_bytes, _stream(stream)))
     return y
+
+
+def fp8_gemm_scaled_fp8out(qa, s_tok, qw, s_ch, q_out=None, s_out=None, y32_out=None, ws=None, stream=None):
+    """FP8-output GEMM: y32 = acc * s_tok * s_ch in fp32, re-quantized per token
+    -> (q_out uint8 [M, N], s_out fp32 [M]); y32_out (fp32 [M, N]) optional."""
+    torch = _torch()
+    M, K, lda = _rows(qa, torch.uint8, "qa")
+    N, K2, ldw = _rows(qw, torch.uint8, "qw")
+    if K2 != K:
+        raise ValueError("qa and qw disagree on K")
+    _vec(s_tok, torch.float32, "s_tok", M)
+    _vec(s_ch, torch.float32, "s_ch", N)
+    if q_out is None:
+        q_out = torch.empty((M, N), dtype=torch.uint8, device=qa.device)
+    _, _, ldq = _rows(q_out, torch.uint8, "q_out")
+    if s_out is None:
+        s_out = torch.empty(M, dtype=torch.float32, device=qa.device)
+    _vec(s_out, torch.float32, "s_out", M)
+    if y32_out is not None:
+        if y32_out.dtype != torch.float32 or tuple(y32_out.shape) != (M, N) or not y32_out.is_contiguous():
+            raise ValueError("y32_out: expected a contiguous float32 [M, N] tensor")
+    if ws is None:
+        need = fp8_fp8out_workspace_bytes(M, N, K)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=qa.device)
+    ws_bytes = ws.numel() * ws.element_size()
+    _check("fp8_gemm_scaled_fp8out",
+           lib().fp8_gemm_scaled_fp8out(_ptr(qa), lda, _ptr(s_tok), _ptr(qw), ldw, _ptr(s_ch), _ptr(q_out), ldq,
+                                        _ptr(s_out), _ptr(y32_out), M, N, K, _ptr(ws), ws_bytes, _stream(stream)))
+    return q_out, s_out
 
 
 def fp8_gemm_grouped_scaled(qa, s_tok, row_token, expert_offsets, qw, s_ch, y=None, ws=None, stream=None):

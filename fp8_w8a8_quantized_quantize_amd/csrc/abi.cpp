@@ -84,15 +84,19 @@ size_t fused_stage_bytes(int64_t M, int64_t K) {
     return round_up((size_t)M * (size_t)K, kAlign) + round_up((size_t)M * sizeof(float), kAlign);
 }
 
+// BF16 output to y, or (y32 != nullptr) the fp32 value before rounding to y32.
 fp8_status_t gemm_dispatch(const uint8_t* qa, int64_t lda, const float* s_tok, const uint8_t* qw, int64_t ldw,
-                           const float* s_ch, uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                           const float* s_ch, uint16_t* y, float* y32, int64_t ldy, int64_t M, int64_t N, int64_t K,
                            void* ws, hipStream_t stream) {
     if (M <= fp8k::kSkinnyMaxM)
-        return from_hip(fp8k::launch_gemm_skinny(qa, lda, s_tok, qw, ldw, s_ch, y, ldy, M, N, K, ws, stream));
+        return from_hip(fp8k::launch_gemm_skinny(qa, lda, s_tok, qw, ldw, s_ch, y, y32, ldy, M, N, K, ws, stream));
     if (K % 128 == 0)
-        return from_hip(fp8k::launch_gemm_mfma(qa, lda, s_tok, qw, ldw, s_ch, y, ldy, M, N, K, stream));
-    return from_hip(fp8k::launch_gemm_tiled(qa, lda, s_tok, qw, ldw, s_ch, y, ldy, M, N, K, stream));
+        return from_hip(fp8k::launch_gemm_mfma(qa, lda, s_tok, qw, ldw, s_ch, y, y32, ldy, M, N, K, stream));
+    return from_hip(fp8k::launch_gemm_tiled(qa, lda, s_tok, qw, ldw, s_ch, y, y32, ldy, M, N, K, stream));
 }
+
+// Bytes of the fp32 output staged by the FP8-output GEMM.
+size_t fp8out_stage_bytes(int64_t M, int64_t N) { return round_up((size_t)M * (size_t)N * sizeof(float), kAlign); }
 
 }  // namespace
 
@@ -114,6 +118,13 @@ size_t fp8_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     int64_t mk;
     if (!mul_ok(M, K, &mk)) return SIZE_MAX;
     return fused_stage_bytes(M, K) + gemm_ws_bytes(M, N, K);
+}
+
+size_t fp8_fp8out_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (check_dims(M, N, K) == FP8_ERR_INVALID_ARGUMENT) return SIZE_MAX;
+    int64_t mn;
+    if (!mul_ok(M, N, &mn) || mn > INT64_MAX / 8) return SIZE_MAX;
+    return fp8out_stage_bytes(M, N) + gemm_ws_bytes(M, N, K);
 }
 
 size_t fp8_grouped_workspace_bytes(int64_t T, int64_t R, int64_t E, int64_t N, int64_t K) {
@@ -147,7 +158,7 @@ fp8_status_t fp8_gemm_scaled(const uint8_t* qa, int64_t lda, const float* s_tok,
     if (need > 0 && ws == nullptr) return FP8_ERR_INVALID_ARGUMENT;
     if (need > 0 && !aligned16(ws)) return FP8_ERR_UNSUPPORTED;
     if (M == 0 || N == 0) return FP8_OK;
-    return gemm_dispatch(qa, lda, s_tok, qw, ldw, s_ch, y, ldy, M, N, K, ws, stream);
+    return gemm_dispatch(qa, lda, s_tok, qw, ldw, s_ch, y, nullptr, ldy, M, N, K, ws, stream);
 }
 
 fp8_status_t fp8_quant_gemm_fused(const float* x, int64_t ldx, const uint8_t* qw, int64_t ldw,
@@ -175,7 +186,37 @@ fp8_status_t fp8_quant_gemm_fused(const float* x, int64_t ldx, const uint8_t* qw
     float* s_tok = s_tok_out ? s_tok_out : reinterpret_cast<float*>(base + round_up((size_t)M * (size_t)K, kAlign));
     FP8_TRY(from_hip(fp8k::launch_quantize_rows(x, ldx, qa, K, s_tok, M, K, stream)));
     if (N == 0) return FP8_OK;
-    return gemm_dispatch(qa, K, s_tok, qw, ldw, s_ch, y, ldy, M, N, K, base + fused_stage_bytes(M, K), stream);
+    return gemm_dispatch(qa, K, s_tok, qw, ldw, s_ch, y, nullptr, ldy, M, N, K, base + fused_stage_bytes(M, K),
+                         stream);
+}
+
+fp8_status_t fp8_gemm_scaled_fp8out(const uint8_t* qa, int64_t lda, const float* s_tok, const uint8_t* qw,
+                                    int64_t ldw, const float* s_ch, uint8_t* q_out, int64_t ldq, float* s_out,
+                                    float* y32_out, int64_t M, int64_t N, int64_t K, void* ws, size_t ws_bytes,
+                                    hipStream_t stream) {
+    FP8_TRY(check_dims(M, N, K));
+    if (N % 16 != 0) return FP8_ERR_UNSUPPORTED;  // output rows are quantized in 16-byte pieces
+    FP8_TRY(check_matrix(qa, M, K, lda, 1));
+    FP8_TRY(check_matrix(qw, N, K, ldw, 1));
+    FP8_TRY(check_vector(s_tok, M));
+    FP8_TRY(check_vector(s_ch, N));
+    FP8_TRY(check_matrix(q_out, M, N, ldq, 1));
+    FP8_TRY(check_vector(s_out, M));
+    if (y32_out) FP8_TRY(check_matrix(y32_out, M, N, N, 4));
+    if (M > 0 && N > 0 && K > 0 && (qa == nullptr || qw == nullptr)) return FP8_ERR_INVALID_ARGUMENT;
+    int64_t mn;
+    if (!mul_ok(M, N, &mn) || mn > INT64_MAX / 8) return FP8_ERR_INVALID_ARGUMENT;
+    const size_t stage = y32_out ? 0 : fp8out_stage_bytes(M, N);
+    const size_t need = stage + gemm_ws_bytes(M, N, K);
+    if (ws_bytes < need) return FP8_ERR_WORKSPACE;
+    if (need > 0 && ws == nullptr) return FP8_ERR_INVALID_ARGUMENT;
+    if (need > 0 && !aligned16(ws)) return FP8_ERR_UNSUPPORTED;
+    if (M == 0) return FP8_OK;
+    float* y32 = y32_out ? y32_out : static_cast<float*>(ws);
+    if (N > 0)
+        FP8_TRY(gemm_dispatch(qa, lda, s_tok, qw, ldw, s_ch, nullptr, y32, N, M, N, K,
+                              static_cast<uint8_t*>(ws) + stage, stream));
+    return from_hip(fp8k::launch_quantize_rows(y32, N, q_out, ldq, s_out, M, N, stream));
 }
 
 fp8_status_t fp8_gemm_grouped_scaled(const uint8_t* qa, const float* s_tok, const int32_t* row_token,

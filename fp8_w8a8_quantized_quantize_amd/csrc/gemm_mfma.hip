@@ -128,6 +128,7 @@ struct MfmaArgs {
     int64_t ldw;
     const float* s_ch;
     uint16_t* y;
+    float* y32;  // when set: fp32 output (unrounded acc * s_tok * s_ch) instead of y, row stride ldy
     int64_t ldy;
     int M, N, K;
     int tiles_m, tiles_n;
@@ -429,6 +430,41 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_mfma_kernel(MfmaArgs p) 
     // written out with 16-byte row-contiguous stores.
     // Accumulator layout of a 32x32 MFMA tile: lane l holds activation row
     // l % 32 and weight columns 8 * (v / 4) + 4 * (l / 32) + v % 4, v = 0..15.
+    if constexpr (!GROUPED) {
+        if (p.y32 != nullptr) {
+            // fp32 output straight from the accumulators: lane l holds 4
+            // consecutive columns per group q (one 16-byte store when aligned).
+            const bool vec = (p.ldy & 3) == 0;
+#pragma unroll
+            for (int b = 0; b < FM; ++b) {
+                const int ml = wm * (BM / WM) + b * 32 + r32;
+                if (ml >= rows_valid) continue;
+                const float st = s_tok_t[ml];
+                float* yr = p.y32 + (int64_t)(m0 + ml) * p.ldy;
+#pragma unroll
+                for (int a = 0; a < FN; ++a) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int nl = wn * (BN / WN) + a * 32 + 8 * q + 4 * g;
+                        const int n = n0 + nl;
+                        if (n >= p.N) continue;
+                        const float4 sc4 = *reinterpret_cast<const float4*>(s_ch_t + nl);
+                        const float o0 = acc[a][b][4 * q + 0] * (st * sc4.x), o1 = acc[a][b][4 * q + 1] * (st * sc4.y);
+                        const float o2 = acc[a][b][4 * q + 2] * (st * sc4.z), o3 = acc[a][b][4 * q + 3] * (st * sc4.w);
+                        if (vec && n + 3 < p.N) {
+                            *reinterpret_cast<float4*>(yr + n) = make_float4(o0, o1, o2, o3);
+                        } else {
+                            if (n < p.N) yr[n] = o0;
+                            if (n + 1 < p.N) yr[n + 1] = o1;
+                            if (n + 2 < p.N) yr[n + 2] = o2;
+                            if (n + 3 < p.N) yr[n + 3] = o3;
+                        }
+                    }
+                }
+            }
+            return;
+        }
+    }
     wait_lds_reads();
     block_barrier();
     uint8_t* ct = smem;
@@ -476,13 +512,13 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_mfma_kernel(MfmaArgs p) 
 }
 
 hipError_t launch_gemm_mfma(const uint8_t* qa, int64_t lda, const float* s_tok, const uint8_t* qw, int64_t ldw,
-                            const float* s_ch, uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                            const float* s_ch, uint16_t* y, float* y32, int64_t ldy, int64_t M, int64_t N, int64_t K,
                             hipStream_t stream) {
     if (M <= 0 || N <= 0) return hipSuccess;
     constexpr int BN = 256, BM = 256, WN = 2, WM = 2;
     constexpr int LDS = 2 * (BN + BM) * kBK + 4 * (BN + BM);  // ring + tile scales
     MfmaArgs p{};
-    p.qa = qa; p.lda = lda; p.s_tok = s_tok; p.qw = qw; p.ldw = ldw; p.s_ch = s_ch; p.y = y; p.ldy = ldy;
+    p.qa = qa; p.lda = lda; p.s_tok = s_tok; p.qw = qw; p.ldw = ldw; p.s_ch = s_ch; p.y = y; p.y32 = y32; p.ldy = ldy;
     p.M = (int)M; p.N = (int)N; p.K = (int)K;
     p.tiles_m = (int)((M + BM - 1) / BM);
     p.tiles_n = (int)((N + BN - 1) / BN);

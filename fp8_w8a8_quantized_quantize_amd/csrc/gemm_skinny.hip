@@ -38,7 +38,8 @@ template <int MT, int NT, int KW, int DEPTH>
 __global__ __launch_bounds__(KW * 64) void gemm_skinny_kernel(
     const uint8_t* __restrict__ qa, int64_t lda, const float* __restrict__ s_tok,
     const uint8_t* __restrict__ qw, int64_t ldw, const float* __restrict__ s_ch,
-    uint16_t* __restrict__ y, int64_t ldy, int M, int N, int K, float* __restrict__ part, int split_chunks) {
+    uint16_t* __restrict__ y, float* __restrict__ y32, int64_t ldy, int M, int N, int K, float* __restrict__ part,
+    int split_chunks) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int r16 = lane & 15;
@@ -149,6 +150,17 @@ __global__ __launch_bounds__(KW * 64) void gemm_skinny_kernel(
             continue;
         }
         const float st = s_tok[m];
+        if (y32 != nullptr) {  // fp32 output: acc * (s_tok * s_ch), unrounded
+            float* yr = y32 + (int64_t)m * ldy;
+            if (nb + 3 < N && (ldy & 3) == 0) {
+                const float4 sc = *reinterpret_cast<const float4*>(s_ch + nb);
+                *reinterpret_cast<float4*>(yr + nb) =
+                    make_float4(sum[0] * (st * sc.x), sum[1] * (st * sc.y), sum[2] * (st * sc.z), sum[3] * (st * sc.w));
+            } else {
+                for (int v = 0; v < 4 && nb + v < N; ++v) yr[nb + v] = sum[v] * (st * s_ch[nb + v]);
+            }
+            continue;
+        }
         uint16_t* yr = y + (int64_t)m * ldy;
         if (nb + 3 < N && (ldy & 3) == 0) {
             const float4 sc = *reinterpret_cast<const float4*>(s_ch + nb);
@@ -341,7 +353,7 @@ __global__ __launch_bounds__(KW * 64) void gemm_skinny_fused_kernel(
 __global__ __launch_bounds__(256) void skinny_splitk_reduce(const float* __restrict__ part, int splits, int M, int N,
                                                            const float* __restrict__ s_tok,
                                                            const float* __restrict__ s_ch, uint16_t* __restrict__ y,
-                                                           int64_t ldy) {
+                                                           float* __restrict__ y32, int64_t ldy) {
     const int n4 = (N + 3) >> 2;
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (t >= (int64_t)M * n4) return;
@@ -350,7 +362,6 @@ __global__ __launch_bounds__(256) void skinny_splitk_reduce(const float* __restr
     const int64_t plane = (int64_t)M * N;
     const float* p = part + (int64_t)m * N + nb;
     const float st = s_tok[m];
-    uint16_t* yr = y + (int64_t)m * ldy;
     if (nb + 3 < N && (N & 3) == 0 && (ldy & 3) == 0) {
         float4 a = *reinterpret_cast<const float4*>(p);
         for (int z = 1; z < splits; ++z) {
@@ -361,6 +372,12 @@ __global__ __launch_bounds__(256) void skinny_splitk_reduce(const float* __restr
             a.w += b.w;
         }
         const float4 sc = *reinterpret_cast<const float4*>(s_ch + nb);
+        if (y32 != nullptr) {
+            *reinterpret_cast<float4*>(y32 + (int64_t)m * ldy + nb) =
+                make_float4(a.x * (st * sc.x), a.y * (st * sc.y), a.z * (st * sc.z), a.w * (st * sc.w));
+            return;
+        }
+        uint16_t* yr = y + (int64_t)m * ldy;
         uint2 o;
         o.x = pack_bf16x2(a.x * (st * sc.x), a.y * (st * sc.y));
         o.y = pack_bf16x2(a.z * (st * sc.z), a.w * (st * sc.w));
@@ -369,29 +386,32 @@ __global__ __launch_bounds__(256) void skinny_splitk_reduce(const float* __restr
         for (int v = 0; v < 4 && nb + v < N; ++v) {
             float a = p[v];
             for (int z = 1; z < splits; ++z) a += p[z * plane + v];
-            yr[nb + v] = (uint16_t)bf16_rne_bits(a * (st * s_ch[nb + v]));
+            if (y32 != nullptr)
+                y32[(int64_t)m * ldy + nb + v] = a * (st * s_ch[nb + v]);
+            else
+                y[(int64_t)m * ldy + nb + v] = (uint16_t)bf16_rne_bits(a * (st * s_ch[nb + v]));
         }
     }
 }
 
 template <int MT, int NT, int KW>
 static void launch_cfg(dim3 grid, hipStream_t stream, const uint8_t* qa, int64_t lda, const float* s_tok,
-                       const uint8_t* qw, int64_t ldw, const float* s_ch, uint16_t* y, int64_t ldy, int M, int N,
-                       int K, float* part, int split_chunks) {
+                       const uint8_t* qw, int64_t ldw, const float* s_ch, uint16_t* y, float* y32, int64_t ldy, int M,
+                       int N, int K, float* part, int split_chunks) {
     constexpr int DEPTH = (MT * NT <= 2) ? 4 : 2;
     hipLaunchKernelGGL((gemm_skinny_kernel<MT, NT, KW, DEPTH>), grid, dim3(KW * 64), 0, stream, qa, lda, s_tok, qw,
-                       ldw, s_ch, y, ldy, M, N, K, part, split_chunks);
+                       ldw, s_ch, y, y32, ldy, M, N, K, part, split_chunks);
 }
 
 template <int MT>
 static void launch_mt(int nt, dim3 grid, hipStream_t stream, const uint8_t* qa, int64_t lda, const float* s_tok,
-                      const uint8_t* qw, int64_t ldw, const float* s_ch, uint16_t* y, int64_t ldy, int M, int N,
-                      int K, float* part, int split_chunks) {
+                      const uint8_t* qw, int64_t ldw, const float* s_ch, uint16_t* y, float* y32, int64_t ldy, int M,
+                      int N, int K, float* part, int split_chunks) {
     switch (nt) {
-        case 8: launch_cfg<MT, 8, 4>(grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, ldy, M, N, K, part, split_chunks); break;
-        case 4: launch_cfg<MT, 4, 8>(grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, ldy, M, N, K, part, split_chunks); break;
-        case 2: launch_cfg<MT, 2, 8>(grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, ldy, M, N, K, part, split_chunks); break;
-        default: launch_cfg<MT, 1, 8>(grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, ldy, M, N, K, part, split_chunks); break;
+        case 8: launch_cfg<MT, 8, 4>(grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, y32, ldy, M, N, K, part, split_chunks); break;
+        case 4: launch_cfg<MT, 4, 8>(grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, y32, ldy, M, N, K, part, split_chunks); break;
+        case 2: launch_cfg<MT, 2, 8>(grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, y32, ldy, M, N, K, part, split_chunks); break;
+        default: launch_cfg<MT, 1, 8>(grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, y32, ldy, M, N, K, part, split_chunks); break;
     }
 }
 
@@ -453,7 +473,7 @@ size_t gemm_skinny_ws_bytes(int64_t M, int64_t N, int64_t K) {
 }
 
 hipError_t launch_gemm_skinny(const uint8_t* qa, int64_t lda, const float* s_tok, const uint8_t* qw,
-                              int64_t ldw, const float* s_ch, uint16_t* y, int64_t ldy, int64_t M, int64_t N,
+                              int64_t ldw, const float* s_ch, uint16_t* y, float* y32, int64_t ldy, int64_t M, int64_t N,
                               int64_t K, void* ws, hipStream_t stream) {
     if (M <= 0 || N <= 0) return hipSuccess;
     const SkinnyPlan p = skinny_plan(M, N, K);
@@ -461,15 +481,15 @@ hipError_t launch_gemm_skinny(const uint8_t* qa, int64_t lda, const float* s_tok
     const dim3 grid((unsigned)((N + 16 * p.nt - 1) / (16 * p.nt)), 1, (unsigned)p.splits);
     const int m = (int)M, n = (int)N, k = (int)K;
     switch (p.mt) {
-        case 1: launch_mt<1>(p.nt, grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, ldy, m, n, k, part, p.split_chunks); break;
-        case 2: launch_mt<2>(p.nt, grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, ldy, m, n, k, part, p.split_chunks); break;
-        case 3: launch_mt<3>(p.nt, grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, ldy, m, n, k, part, p.split_chunks); break;
-        default: launch_mt<4>(p.nt, grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, ldy, m, n, k, part, p.split_chunks); break;
+        case 1: launch_mt<1>(p.nt, grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, y32, ldy, m, n, k, part, p.split_chunks); break;
+        case 2: launch_mt<2>(p.nt, grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, y32, ldy, m, n, k, part, p.split_chunks); break;
+        case 3: launch_mt<3>(p.nt, grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, y32, ldy, m, n, k, part, p.split_chunks); break;
+        default: launch_mt<4>(p.nt, grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, y32, ldy, m, n, k, part, p.split_chunks); break;
     }
     if (part != nullptr) {
         const int64_t threads = M * ((N + 3) / 4);
         hipLaunchKernelGGL(skinny_splitk_reduce, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, part,
-                           p.splits, m, n, s_tok, s_ch, y, ldy);
+                           p.splits, m, n, s_tok, s_ch, y, y32, ldy);
     }
     return hipGetLastError();
 }

@@ -35,6 +35,7 @@ struct TiledArgs {
     int64_t ldw;
     const float* s_ch;
     uint16_t* y;
+    float* y32;  // when set (dense only): fp32 output instead of y, row stride ldy
     int64_t ldy;
     int M, N, K;
     int tiles_m, tiles_n;
@@ -259,6 +260,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(TiledArgs p) {
             const int nb = n0 + wrow0 + a * 16 + 4 * g;
             if (nb >= p.N) continue;
             const v4f s = acc[a][b];
+            if (!GROUPED && p.y32 != nullptr) {
+                float* yr32 = p.y32 + yrow * p.ldy;
+                for (int v = 0; v < 4 && nb + v < p.N; ++v) yr32[nb + v] = s[v] * (st * s_ch[nb + v]);
+                continue;
+            }
             if (nb + 3 < p.N && vec_store) {
                 const float4 sc = *reinterpret_cast<const float4*>(s_ch + nb);
                 uint2 o;
@@ -274,12 +280,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(TiledArgs p) {
 }
 
 hipError_t launch_gemm_tiled(const uint8_t* qa, int64_t lda, const float* s_tok, const uint8_t* qw,
-                             int64_t ldw, const float* s_ch, uint16_t* y, int64_t ldy, int64_t M, int64_t N,
+                             int64_t ldw, const float* s_ch, uint16_t* y, float* y32, int64_t ldy, int64_t M, int64_t N,
                              int64_t K, hipStream_t stream) {
     if (M <= 0 || N <= 0) return hipSuccess;
     constexpr int BN = 256, BM = 256;
     TiledArgs p{};
-    p.qa = qa; p.lda = lda; p.s_tok = s_tok; p.qw = qw; p.ldw = ldw; p.s_ch = s_ch; p.y = y; p.ldy = ldy;
+    p.qa = qa; p.lda = lda; p.s_tok = s_tok; p.qw = qw; p.ldw = ldw; p.s_ch = s_ch; p.y = y; p.y32 = y32; p.ldy = ldy;
     p.M = (int)M; p.N = (int)N; p.K = (int)K;
     p.tiles_m = (int)((M + BM - 1) / BM);
     p.tiles_n = (int)((N + BN - 1) / BN);

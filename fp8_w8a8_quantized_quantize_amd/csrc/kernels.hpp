@@ -12,6 +12,9 @@ namespace fp8k {
 hipError_t launch_quantize_rows(const float* x, int64_t ldx, uint8_t* q, int64_t ldq, float* scales,
                                 int64_t rows, int64_t K, hipStream_t stream);
 
+// The dense GEMM launchers write BF16 y, or, when y32 is not null, the fp32
+// value acc * (s_tok * s_ch) before rounding to y32 (same row stride ldy).
+
 // Largest M the skinny (decode) kernel takes.
 constexpr int64_t kSkinnyMaxM = 64;
 
@@ -25,7 +28,7 @@ struct SkinnyPlan {
 SkinnyPlan skinny_plan(int64_t M, int64_t N, int64_t K);
 size_t gemm_skinny_ws_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_skinny(const uint8_t* qa, int64_t lda, const float* s_tok, const uint8_t* qw,
-                              int64_t ldw, const float* s_ch, uint16_t* y, int64_t ldy, int64_t M, int64_t N,
+                              int64_t ldw, const float* s_ch, uint16_t* y, float* y32, int64_t ldy, int64_t M, int64_t N,
                               int64_t K, void* ws, hipStream_t stream);
 
 // Quantize + skinny GEMM in one kernel, for M <= kSkinnyFusedMaxM rows whose
@@ -40,12 +43,12 @@ hipError_t launch_gemm_skinny_fused(const float* x, int64_t ldx, const uint8_t* 
 
 // LDS-tiled MFMA scaled GEMM for larger M (gemm_tiled.hip).
 hipError_t launch_gemm_tiled(const uint8_t* qa, int64_t lda, const float* s_tok, const uint8_t* qw,
-                             int64_t ldw, const float* s_ch, uint16_t* y, int64_t ldy, int64_t M, int64_t N,
+                             int64_t ldw, const float* s_ch, uint16_t* y, float* y32, int64_t ldy, int64_t M, int64_t N,
                              int64_t K, hipStream_t stream);
 
 // Two-stage DMA-fed MFMA GEMM, K % 128 == 0 (gemm_mfma.hip).
 hipError_t launch_gemm_mfma(const uint8_t* qa, int64_t lda, const float* s_tok, const uint8_t* qw, int64_t ldw,
-                            const float* s_ch, uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                            const float* s_ch, uint16_t* y, float* y32, int64_t ldy, int64_t M, int64_t N, int64_t K,
                             hipStream_t stream);
 
 // Grouped (MoE) variant of the two-stage kernel, K % 128 == 0 (gemm_mfma.hip).

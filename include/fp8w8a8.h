@@ -119,6 +119,31 @@ fp8_status_t fp8_quant_gemm_fused(const float* x, int64_t ldx, const uint8_t* qw
                                   void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * FP8-output scaled GEMM: the dataflow of the DeepSeek V4 950 page, §2.3
+ * (FP8 inputs, FP32 accumulation, the output converted back to FP8 for the
+ * next layer), with the output re-quantized per token like the activations:
+ *   y32[m,n]  = fl32( (sum_k e4m3(qa[m,k]) * e4m3(qw[n,k])) * (s_tok[m] * s_ch[n]) )
+ *               (the fp32 value fp8_gemm_scaled rounds to BF16)
+ *   s_out[m]  = max(fl32(max_n |y32[m,n]| / 448), 1e-12f)
+ *   q_out[m,n] = E4M3 code of fl32(y32[m,n] / s_out[m]), RNE, saturating +-448
+ * so q_out / s_out can feed the next layer's qa / s_tok directly.
+ * q_out: u8 [M, N], stride ldq; s_out: fp32 [M].  y32_out (fp32 [M, N],
+ * stride N) is optional: when given it receives y32 and serves as the
+ * staging buffer, else y32 is staged in ws.  N must be a multiple of 16
+ * (FP8_ERR_UNSUPPORTED otherwise).  ws must hold at least
+ * fp8_fp8out_workspace_bytes(M, N, K) bytes (M * N * 4 fewer when y32_out is
+ * given).  The FP32 accumulation order is the GEMM kernels' own, so a code can
+ * differ from one computed from the exact sum where y32 lies within rounding
+ * error of an E4M3 rounding boundary; the codes are exactly those of
+ * fp8_quantize_per_token applied to y32.
+ */
+fp8_status_t fp8_gemm_scaled_fp8out(const uint8_t* qa, int64_t lda, const float* s_tok,
+                                    const uint8_t* qw, int64_t ldw, const float* s_ch,
+                                    uint8_t* q_out, int64_t ldq, float* s_out, float* y32_out,
+                                    int64_t M, int64_t N, int64_t K,
+                                    void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * Grouped (MoE expert) scaled FP8 GEMM (DeepSeek V4 950 page, §2.3 item 5:
  * expert computation entirely in FP8; §2.4 per-channel scales per expert).
  * Routed rows are sorted by expert: rows [expert_offsets[e], expert_offsets[e+1])
@@ -138,6 +163,10 @@ fp8_status_t fp8_gemm_grouped_scaled(const uint8_t* qa, const float* s_tok,
                                      const uint8_t* qw, const float* s_ch, uint16_t* y,
                                      int64_t T, int64_t R, int64_t E, int64_t N, int64_t K,
                                      void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes fp8_gemm_scaled_fp8out needs (host only; SIZE_MAX for
+ * invalid sizes). */
+size_t fp8_fp8out_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* Workspace bytes fp8_gemm_scaled and fp8_quant_gemm_fused need for this
  * shape (host-only, pure; 0 when none is needed; SIZE_MAX for invalid sizes). */

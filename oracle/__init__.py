@@ -10,7 +10,9 @@ a plain C implementation written from the FP8 pages:
     V4 950 page §2.4 and §3.1 describe);
   - the FP8 x FP8 GEMM with wide accumulation and s_tok*s_ch rescale
     (DeepSeek V4 950 page §2.3), exact in binary64;
-  - the grouped (MoE expert) variant of that GEMM.
+  - the grouped (MoE expert) variant of that GEMM;
+  - the FP8-output form of the GEMM (the output converted back to FP8, DeepSeek
+    V4 950 page §2.3), composed from the exact GEMM and the quantizer.
 It shares no code with the HIP library.  Every function is pinned by the
 `-m "not gpu"` tests against the pages' fixed points, PyTorch's float8_e4m3fn
 cast, brute force and exact integer arithmetic.
@@ -145,6 +147,17 @@ def grouped_ref_sampled(qa, s_tok, row_token, offsets, qw, s_ch, rs, ns):
     if rc != 0:
         raise ValueError("a sampled row lies outside every expert's range")
     return ref, ab
+
+
+def fp8out_ref(qa, s_tok, qw, s_ch):
+    """FP8-output GEMM from the definition (DeepSeek V4 950 page, §2.3: the FP32
+    result converted back to FP8; per-token scales as for the activations,
+    §2.4 and §3.1): y = the exact scaled product rounded once to fp32, then the
+    per-row absmax quantizer on y.  Returns (y32 float32 [M,N], codes, scales)."""
+    ref, _ = gemm_ref(qa, s_tok, qw, s_ch)
+    y32 = ref.astype(np.float32)
+    q, s = quantize_rows(y32)
+    return y32, q, s
 
 
 def bf16_from_double(v):

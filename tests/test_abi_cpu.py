@@ -49,6 +49,41 @@ def test_workspace_bytes():
     assert fp8.fp8_workspace_bytes(0, 5, 16) == 0
     assert fp8.fp8_workspace_bytes(-1, 5, 16) == ctypes.c_size_t(-1).value
     assert fp8.fp8_grouped_workspace_bytes(4096, 32768, 64, 2048, 7168) == 0
+    # split-K decode shape: fp32 partial sums for 4 splits follow the staged codes
+    assert fp8.fp8_workspace_bytes(64, 8192, 28672) == 64 * 28672 + 256 + 4 * 64 * 8192 * 4
+    # FP8-output GEMM: the fp32 output staged (256-byte rounded), then the GEMM's own needs
+    assert fp8.fp8_fp8out_workspace_bytes(8, 14336, 4096) == 8 * 14336 * 4
+    assert fp8.fp8_fp8out_workspace_bytes(64, 8192, 28672) == 64 * 8192 * 4 + 4 * 64 * 8192 * 4
+    assert fp8.fp8_fp8out_workspace_bytes(-1, 5, 16) == ctypes.c_size_t(-1).value
+
+
+def fo(*a):
+    return fp8.lib().fp8_gemm_scaled_fp8out(*a)
+
+
+def test_fp8out_validation():
+    # qa, lda, s_tok, qw, ldw, s_ch, q_out, ldq, s_out, y32_out, M, N, K, ws, ws_bytes, stream
+    need = fp8.fp8_fp8out_workspace_bytes(4, 32, 64)
+    base = [P, 64, P, Q, 64, P, Q, 32, P, 0, 4, 32, 64, P, need, S0]
+
+    def with_(**kw):
+        a = list(base)
+        idx = dict(qa=0, lda=1, st=2, qw=3, ldw=4, sc=5, qo=6, ldq=7, so=8, y32=9, M=10, N=11, K=12, ws=13, wsb=14)
+        for k, v in kw.items():
+            a[idx[k]] = v
+        return fo(*a)
+
+    assert with_(N=40, ldq=48) == FP8_ERR_UNSUPPORTED            # output rows must be 16-multiples
+    assert with_(K=40, lda=48, ldw=48) == FP8_ERR_UNSUPPORTED
+    assert with_(wsb=need - 1) == FP8_ERR_WORKSPACE
+    assert with_(ws=0) == FP8_ERR_INVALID_ARGUMENT
+    assert with_(ws=MIS) == FP8_ERR_UNSUPPORTED
+    assert with_(qo=0) == FP8_ERR_INVALID_ARGUMENT
+    assert with_(so=0) == FP8_ERR_INVALID_ARGUMENT
+    assert with_(ldq=24) == FP8_ERR_INVALID_ARGUMENT              # ldq < N
+    assert with_(ldq=40) == FP8_ERR_UNSUPPORTED                   # code rows not 16-byte strided
+    assert with_(y32=MIS) == FP8_ERR_UNSUPPORTED
+    assert with_(M=0, qa=0, st=0, qo=0, so=0) == FP8_OK          # empty: no-op
 
 
 def q(*a):
