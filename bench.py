@@ -59,6 +59,9 @@ def parse():
     ap.add_argument("--out", choices=("bf16", "fp8"), default="bf16",
                     help="bf16: the fused quantize+GEMM step (default); fp8: the FP8-output GEMM "
                          "(fp8_gemm_scaled_fp8out on FP8 activations, dense workloads)")
+    ap.add_argument("--act", choices=("dynamic", "static", "clipped"), default="dynamic",
+                    help="activation scales: per-token absmax (default, the fused call), a static per-tensor "
+                         "scale calibrated as the P99.9 of |x|, or per-token scales clipped at the P99.99 of |x|")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run 5 plain device copies of 512 MiB (reference for rocprofv3 FETCH/WRITE_SIZE)")
     ap.add_argument("--profile", action="store_true",
@@ -228,6 +231,29 @@ def main():
         def step(i):
             fp8.fp8_quant_gemm_fused(xd, wcopies[i % copies], sc, y=y, ws=ws)
 
+        calib = None
+        if args.act != "dynamic":
+            # offline calibration on the same activations, timed once on its own
+            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            num, den = (999, 1000) if args.act == "static" else (9999, 10000)
+            fp8.fp8_calibrate_percentile(xd, num, den)
+            c0.record()
+            value, sscale = fp8.fp8_calibrate_percentile(xd, num, den)
+            c1.record()
+            torch.cuda.synchronize()
+            cal_ms = c0.elapsed_time(c1)
+            calib = dict(percentile=f"{num}/{den}", value=float(value.cpu()[0]), scale=float(sscale.cpu()[0]),
+                         calibrate_us=round(cal_ms * 1e3, 3), calibrate_gbs=round(4 * M * K / (cal_ms * 1e-3) / 1e9, 1))
+            qs = torch.empty((M, K), dtype=torch.uint8, device=dev)
+            ss = torch.empty(M, dtype=torch.float32, device=dev)
+
+            def step(i):
+                if args.act == "static":
+                    fp8.fp8_quantize_static(xd, sscale, q=qs, scales_out=ss)
+                else:
+                    fp8.fp8_quantize_per_token_clipped(xd, value, q=qs, scales=ss)
+                fp8.fp8_gemm_scaled(qs, ss, wcopies[i % copies], sc, y=y, ws=ws)
+
         # the dominant kernel alone: the GEMM on pre-quantized activations
         fp8.fp8_quantize_per_token(xd, q=qa, scales=st)
 
@@ -245,10 +271,12 @@ def main():
         gemm_avg_ms = gemm_ms / steps
         kind = "skinny" if decode else "mfma"
         # The library runs the fused call as one kernel (quantization in the
-        # GEMM's prologue) for M <= 16 rows whose codes fit in LDS and whose
-        # fp32 values fit in 16 float4 registers per lane (include/fp8w8a8.h);
-        # then that kernel is the whole step and is the one the roofline rates.
-        one_kernel = M <= 16 and M * (K + 16) <= 64 * 1024 + 256 and -(-K // 256) <= (16 if M <= 8 else 8)
+        # GEMM's prologue) for M <= 16 rows whose codes fit in LDS, whose fp32
+        # values fit in 16 float4 registers per lane, and N <= 8192
+        # (include/fp8w8a8.h); then that kernel is the whole step and is the
+        # one the roofline rates.
+        one_kernel = (args.act == "dynamic" and M <= 16 and M * (K + 16) <= 64 * 1024 + 256
+                      and -(-K // 256) <= (16 if M <= 8 else 8) and 0 < N <= 8192)
         gemm_only = None
         if decode:
             value, unit = step_bytes / (ms * 1e-3) / 1e9, "GB/s"
@@ -278,10 +306,14 @@ def main():
             roof["avg_launch_us"] = round(gemm_avg_ms * 1e3, 3)
         roof["traffic"] = read_traffic(args.workload, kind, roof["kernel"])
         cfg = dict(workload=args.workload, M=M, N=N, K=K, seed=args.seed, weight_copies=copies,
-                   step="fp8_quant_gemm_fused", out="bf16")
+                   step=("fp8_quant_gemm_fused" if args.act == "dynamic" else
+                         ("fp8_quantize_static" if args.act == "static" else "fp8_quantize_per_token_clipped")
+                         + " + fp8_gemm_scaled"), act_scales=args.act, out="bf16")
         extra = dict(timing="hip-graph replay of the steps" if graph else "eager launches",
                      step_us=round(ms * 1e3, 3), step_tflops=round(flops / (ms * 1e-3) / 1e12, 2),
                      step_gbs=round(step_bytes / (ms * 1e-3) / 1e9, 1))
+        if calib:
+            extra["calibration"] = calib
         if per:
             extra.update(step_us_median=round(pct(per, 0.5) * 1e3, 3), step_us_p10=round(pct(per, 0.1) * 1e3, 3),
                          step_us_p90=round(pct(per, 0.9) * 1e3, 3), gemm_us_median=round(pct(gemm_per, 0.5) * 1e3, 3))

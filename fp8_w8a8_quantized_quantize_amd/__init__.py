@@ -8,6 +8,9 @@ if the library is missing, importing a function raises.
 
 Entry points (same names as the C ABI):
   fp8_quantize_per_token(x)                -> (q uint8 [M,K], scales fp32 [M])
+  fp8_quantize_static(x, scale)            -> (q, scales)   static per-tensor scale (device fp32 [1])
+  fp8_quantize_per_token_clipped(x, clip)  -> (q, scales)   per-token scale, absmax clipped at *clip
+  fp8_calibrate_percentile(x, num, den)    -> (value fp32 [1], scale fp32 [1])  nearest-rank |x| percentile
   fp8_gemm_scaled(qa, s_tok, qw, s_ch)     -> y bf16 [M,N]
   fp8_quant_gemm_fused(x, qw, s_ch)        -> y bf16 [M,N]  (optionally qa, s_tok)
   fp8_gemm_scaled_fp8out(qa, s_tok, qw, s_ch) -> (q_out uint8 [M,N], s_out fp32 [M])  (optionally y32)
@@ -28,7 +31,8 @@ FP8_ERR_WORKSPACE = 3
 FP8_ERR_DEVICE = 4
 
 # exported symbols, as declared in include/fp8w8a8.h
-EXPORTS = ("fp8_quantize_per_token", "fp8_gemm_scaled", "fp8_quant_gemm_fused", "fp8_gemm_scaled_fp8out",
+EXPORTS = ("fp8_quantize_per_token", "fp8_quantize_static", "fp8_quantize_per_token_clipped",
+           "fp8_calibrate_percentile", "fp8_calibrate_workspace_bytes", "fp8_gemm_scaled", "fp8_quant_gemm_fused", "fp8_gemm_scaled_fp8out",
            "fp8_gemm_grouped_scaled", "fp8_workspace_bytes", "fp8_fp8out_workspace_bytes",
            "fp8_grouped_workspace_bytes", "fp8_status_string")
 
@@ -52,6 +56,14 @@ def lib():
         i64, vp, sz, st = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
         L.fp8_quantize_per_token.restype = st
         L.fp8_quantize_per_token.argtypes = [vp, i64, i64, i64, vp, i64, vp, vp]
+        L.fp8_quantize_static.restype = st
+        L.fp8_quantize_static.argtypes = [vp, i64, i64, i64, vp, vp, i64, vp, vp]
+        L.fp8_quantize_per_token_clipped.restype = st
+        L.fp8_quantize_per_token_clipped.argtypes = [vp, i64, i64, i64, vp, vp, i64, vp, vp]
+        L.fp8_calibrate_percentile.restype = st
+        L.fp8_calibrate_percentile.argtypes = [vp, i64, i64, i64, vp, vp, vp, sz, vp]
+        L.fp8_calibrate_workspace_bytes.restype = sz
+        L.fp8_calibrate_workspace_bytes.argtypes = []
         L.fp8_gemm_scaled.restype = st
         L.fp8_gemm_scaled.argtypes = [vp, i64, vp, vp, i64, vp, vp, i64, i64, i64, i64, vp, sz, vp]
         L.fp8_quant_gemm_fused.restype = st
@@ -142,6 +154,61 @@ def fp8_quantize_per_token(x, q=None, scales=None, stream=None):
     _check("fp8_quantize_per_token",
            lib().fp8_quantize_per_token(_ptr(x), M, K, ldx, _ptr(q), ldq, _ptr(scales), _stream(stream)))
     return q, scales
+
+
+def _scalar(t, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or not t.is_cuda or t.numel() < 1:
+        raise TypeError(f"{name}: expected a float32 CUDA tensor holding one value")
+
+
+def fp8_quantize_static(x, scale, q=None, scales_out=None, stream=None):
+    """Static per-tensor quantization of fp32 x [M, K] with the device scalar
+    `scale` -> (q uint8 [M, K], scales_out fp32 [M] filled with the scale)."""
+    torch = _torch()
+    M, K, ldx = _rows(x, torch.float32, "x")
+    _scalar(scale, "scale")
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    if scales_out is None:
+        scales_out = torch.empty(M, dtype=torch.float32, device=x.device)
+    _, _, ldq = _rows(q, torch.uint8, "q")
+    _vec(scales_out, torch.float32, "scales_out", M)
+    _check("fp8_quantize_static", lib().fp8_quantize_static(_ptr(x), M, K, ldx, _ptr(scale), _ptr(q), ldq,
+                                                            _ptr(scales_out), _stream(stream)))
+    return q, scales_out
+
+
+def fp8_quantize_per_token_clipped(x, clip, q=None, scales=None, stream=None):
+    """Per-token quantization with the row absmax clipped at the device scalar `clip`."""
+    torch = _torch()
+    M, K, ldx = _rows(x, torch.float32, "x")
+    _scalar(clip, "clip")
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(M, dtype=torch.float32, device=x.device)
+    _, _, ldq = _rows(q, torch.uint8, "q")
+    _vec(scales, torch.float32, "scales", M)
+    _check("fp8_quantize_per_token_clipped",
+           lib().fp8_quantize_per_token_clipped(_ptr(x), M, K, ldx, _ptr(clip), _ptr(q), ldq, _ptr(scales),
+                                                _stream(stream)))
+    return q, scales
+
+
+def fp8_calibrate_percentile(x, num, den, stream=None):
+    """Nearest-rank percentile num/den of |x| over all of x (fp32, contiguous)
+    -> (value fp32 [1], static scale fp32 [1]) on the device."""
+    torch = _torch()
+    if not isinstance(x, torch.Tensor) or x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
+        raise TypeError("x: expected a contiguous float32 CUDA tensor")
+    value = torch.empty(1, dtype=torch.float32, device=x.device)
+    scale = torch.empty(1, dtype=torch.float32, device=x.device)
+    ws = torch.empty(int(lib().fp8_calibrate_workspace_bytes()), dtype=torch.uint8, device=x.device)
+    _check("fp8_calibrate_percentile",
+           lib().fp8_calibrate_percentile(_ptr(x), x.numel(), int(num), int(den), _ptr(value), _ptr(scale), _ptr(ws),
+                                          ws.numel(), _stream(stream)))
+    return value, scale
 
 
 def fp8_gemm_scaled(qa, s_tok, qw, s_ch, y=None, ws=None, stream=None):

@@ -142,6 +142,50 @@ fp8_status_t fp8_quantize_per_token(const float* x, int64_t rows, int64_t K, int
     return from_hip(fp8k::launch_quantize_rows(x, ldx, q, ldq, scales, rows, K, stream));
 }
 
+fp8_status_t fp8_quantize_static(const float* x, int64_t rows, int64_t K, int64_t ldx, const float* scale,
+                                 uint8_t* q, int64_t ldq, float* scales_out, hipStream_t stream) {
+    FP8_TRY(check_dims(rows, 1, K));
+    FP8_TRY(check_matrix(x, rows, K, ldx, 4));
+    FP8_TRY(check_matrix(q, rows, K, ldq, 1));
+    FP8_TRY(check_vector(scales_out, rows));
+    if (rows > 0 && scale == nullptr) return FP8_ERR_INVALID_ARGUMENT;
+    if (rows > 0 && (reinterpret_cast<uintptr_t>(scale) & 3u) != 0) return FP8_ERR_UNSUPPORTED;
+    if (rows == 0) return FP8_OK;
+    return from_hip(fp8k::launch_quantize_static(x, ldx, scale, q, ldq, scales_out, rows, K, stream));
+}
+
+fp8_status_t fp8_quantize_per_token_clipped(const float* x, int64_t rows, int64_t K, int64_t ldx, const float* clip,
+                                            uint8_t* q, int64_t ldq, float* scales, hipStream_t stream) {
+    FP8_TRY(check_dims(rows, 1, K));
+    FP8_TRY(check_matrix(x, rows, K, ldx, 4));
+    FP8_TRY(check_matrix(q, rows, K, ldq, 1));
+    FP8_TRY(check_vector(scales, rows));
+    if (rows > 0 && clip == nullptr) return FP8_ERR_INVALID_ARGUMENT;
+    if (rows > 0 && (reinterpret_cast<uintptr_t>(clip) & 3u) != 0) return FP8_ERR_UNSUPPORTED;
+    if (rows == 0) return FP8_OK;
+    return from_hip(fp8k::launch_quantize_clipped(x, ldx, clip, q, ldq, scales, rows, K, stream));
+}
+
+size_t fp8_calibrate_workspace_bytes(void) { return fp8k::kCalibrateWsBytes; }
+
+fp8_status_t fp8_calibrate_percentile(const float* x, int64_t n, int64_t num, int64_t den, float* value_out,
+                                      float* scale_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (n <= 0 || num <= 0 || den <= 0 || num > den) return FP8_ERR_INVALID_ARGUMENT;
+    if (n > (int64_t)UINT32_MAX) return FP8_ERR_UNSUPPORTED;  // 32-bit histogram bins
+    if (x == nullptr || value_out == nullptr || ws == nullptr) return FP8_ERR_INVALID_ARGUMENT;
+    if ((reinterpret_cast<uintptr_t>(x) & 3u) != 0 || (reinterpret_cast<uintptr_t>(value_out) & 3u) != 0 ||
+        (reinterpret_cast<uintptr_t>(scale_out) & 3u) != 0)
+        return FP8_ERR_UNSUPPORTED;
+    if (!aligned16(ws)) return FP8_ERR_UNSUPPORTED;
+    if (ws_bytes < fp8k::kCalibrateWsBytes) return FP8_ERR_WORKSPACE;
+    // nearest rank: ceil(num * n / den), exact in 128-bit integers
+    const unsigned __int128 prod = (unsigned __int128)num * (unsigned __int128)n;
+    int64_t rank = (int64_t)((prod + (unsigned __int128)(den - 1)) / (unsigned __int128)den);
+    if (rank < 1) rank = 1;
+    if (rank > n) rank = n;
+    return from_hip(fp8k::launch_calibrate_percentile(x, n, rank, value_out, scale_out, ws, stream));
+}
+
 fp8_status_t fp8_gemm_scaled(const uint8_t* qa, int64_t lda, const float* s_tok, const uint8_t* qw,
                              int64_t ldw, const float* s_ch, uint16_t* y, int64_t ldy, int64_t M, int64_t N,
                              int64_t K, void* ws, size_t ws_bytes, hipStream_t stream) {
@@ -178,7 +222,7 @@ fp8_status_t fp8_quant_gemm_fused(const float* x, int64_t ldx, const uint8_t* qw
     if (need > 0 && ws == nullptr) return FP8_ERR_INVALID_ARGUMENT;
     if (need > 0 && !aligned16(ws)) return FP8_ERR_UNSUPPORTED;
     if (M == 0) return FP8_OK;
-    if (N > 0 && fp8k::gemm_skinny_fused_fits(M, K))
+    if (N > 0 && fp8k::gemm_skinny_fused_fits(M, N, K))
         return from_hip(fp8k::launch_gemm_skinny_fused(x, ldx, qw, ldw, s_ch, y, ldy, M, N, K, qa_out, s_tok_out,
                                                        stream));
     uint8_t* base = static_cast<uint8_t*>(ws);

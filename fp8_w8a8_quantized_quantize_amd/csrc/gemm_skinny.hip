@@ -494,8 +494,15 @@ hipError_t launch_gemm_skinny(const uint8_t* qa, int64_t lda, const float* s_tok
     return hipGetLastError();
 }
 
-bool gemm_skinny_fused_fits(int64_t M, int64_t K) {
+// The one-kernel path pays for every workgroup reading all of x (fp32) from
+// L2.  Measured on MI355X against quantize + GEMM in HIP graphs: it wins by
+// 1-1.5 us for N = 4096 and 8192 and loses for N = 14336 (17.6 vs 16.9 us)
+// and 28672 (29.5 vs 27.1 us), so wider outputs take the two-kernel path.
+constexpr int64_t kFusedMaxN = 8192;
+
+bool gemm_skinny_fused_fits(int64_t M, int64_t N, int64_t K) {
     if (M < 1 || M > kSkinnyFusedMaxM || M * (K + kFusedRowPad) > kSkinnyFusedLds) return false;
+    if (N > kFusedMaxN) return false;
     const int64_t vec_per_row = (K / 4 + 63) / 64;
     return vec_per_row <= (M > kFusedWaves ? kFusedRegVec / 2 : kFusedRegVec);
 }
@@ -516,7 +523,7 @@ hipError_t launch_gemm_skinny_fused(const float* x, int64_t ldx, const uint8_t* 
                                     uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K, uint8_t* qa_out,
                                     float* s_tok_out, hipStream_t stream) {
     if (M <= 0 || N <= 0) return hipSuccess;
-    if (!gemm_skinny_fused_fits(M, K)) return hipErrorInvalidValue;
+    if (!gemm_skinny_fused_fits(M, N, K)) return hipErrorInvalidValue;
     // the same weight-rows-per-workgroup rule as the unfused M <= 16 case
     int nt = 1;
     for (int c = 4; c >= 1; c >>= 1)

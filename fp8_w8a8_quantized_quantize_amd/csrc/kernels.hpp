@@ -11,6 +11,19 @@ namespace fp8k {
 // Per-row absmax quantization (quantize.hip).
 hipError_t launch_quantize_rows(const float* x, int64_t ldx, uint8_t* q, int64_t ldq, float* scales,
                                 int64_t rows, int64_t K, hipStream_t stream);
+// Static per-tensor scale *scale (device, floored at 1e-12) for every row;
+// scales[r] receives it for each row.
+hipError_t launch_quantize_static(const float* x, int64_t ldx, const float* scale, uint8_t* q, int64_t ldq,
+                                  float* scales, int64_t rows, int64_t K, hipStream_t stream);
+// Per-row absmax scale with the absmax clipped at *clip (device).
+hipError_t launch_quantize_clipped(const float* x, int64_t ldx, const float* clip, uint8_t* q, int64_t ldq,
+                                   float* scales, int64_t rows, int64_t K, hipStream_t stream);
+// Nearest-rank percentile of |x| over n values (calibrate.hip): value_out =
+// the rank-th smallest |x| (1 <= rank <= n); scale_out (nullable) =
+// max(fl32(value / 448), 1e-12f).  ws: kCalibrateWsBytes bytes.
+constexpr size_t kCalibrateWsBytes = 2048;
+hipError_t launch_calibrate_percentile(const float* x, int64_t n, int64_t rank, float* value_out, float* scale_out,
+                                       void* ws, hipStream_t stream);
 
 // The dense GEMM launchers write BF16 y, or, when y32 is not null, the fp32
 // value acc * (s_tok * s_ch) before rounding to y32 (same row stride ldy).
@@ -32,11 +45,11 @@ hipError_t launch_gemm_skinny(const uint8_t* qa, int64_t lda, const float* s_tok
                               int64_t K, void* ws, hipStream_t stream);
 
 // Quantize + skinny GEMM in one kernel, for M <= kSkinnyFusedMaxM rows whose
-// codes fit in kSkinnyFusedLds bytes of LDS (gemm_skinny.hip).  qa_out and
+// codes fit in kSkinnyFusedLds bytes of LDS and N <= 8192 (gemm_skinny.hip).  qa_out and
 // s_tok_out may be null; when given they receive the codes and scales.
 constexpr int64_t kSkinnyFusedMaxM = 16;
 constexpr int64_t kSkinnyFusedLds = 64 * 1024 + 16 * 16;
-bool gemm_skinny_fused_fits(int64_t M, int64_t K);
+bool gemm_skinny_fused_fits(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_skinny_fused(const float* x, int64_t ldx, const uint8_t* qw, int64_t ldw, const float* s_ch,
                                     uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K, uint8_t* qa_out,
                                     float* s_tok_out, hipStream_t stream);

@@ -37,11 +37,27 @@ __device__ __forceinline__ float block_max(float v, float* red) {
     return r;
 }
 
+// The row scale of each mode: the per-token absmax scale (MODE 0), one static
+// per-tensor scale *param for every row (MODE 1: no absmax is taken), or the
+// per-token absmax scale with the absmax clipped at *param (MODE 2).
+template <int MODE>
+__device__ __forceinline__ RowScale mode_scale(float amax, const float* param) {
+    if constexpr (MODE == 1) {
+        const float s = fmaxf(*param, kScaleFloor);
+        return RowScale{s, __fdiv_rn(1.0f, s)};
+    } else if constexpr (MODE == 2) {
+        return make_row_scale(fminf(amax, *param));
+    } else {
+        return make_row_scale(amax);
+    }
+}
+
 // Row held in registers: VPT float4 per thread, K4 = K / 4 <= T * VPT.
-template <int VPT, int T>
+template <int VPT, int T, int MODE>
 __global__ __launch_bounds__(T) void quantize_rows_regs(const float* __restrict__ x, int64_t ldx,
                                                         uint8_t* __restrict__ q, int64_t ldq,
-                                                        float* __restrict__ scales, int64_t rows, int K4) {
+                                                        float* __restrict__ scales, int64_t rows, int K4,
+                                                        const float* __restrict__ param) {
     __shared__ float red[T / kWave];
     for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
         const float4* xr = reinterpret_cast<const float4*>(x + r * ldx);
@@ -52,11 +68,11 @@ __global__ __launch_bounds__(T) void quantize_rows_regs(const float* __restrict_
             const int j = i * T + threadIdx.x;
             if (j < K4) {
                 v[i] = xr[j];
-                amax = absmax4(amax, v[i]);
+                if constexpr (MODE != 1) amax = absmax4(amax, v[i]);
             }
         }
-        amax = block_max<T>(amax, red);
-        const RowScale rs = make_row_scale(amax);
+        if constexpr (MODE != 1) amax = block_max<T>(amax, red);
+        const RowScale rs = mode_scale<MODE>(amax, param);
         if (threadIdx.x == 0) scales[r] = rs.s;
         uint32_t* qr = reinterpret_cast<uint32_t*>(q + r * ldq);
 #pragma unroll
@@ -68,53 +84,76 @@ __global__ __launch_bounds__(T) void quantize_rows_regs(const float* __restrict_
 }
 
 // Any K: absmax pass, then a second (L2-resident) pass for the cast.
-template <int T>
+template <int T, int MODE>
 __global__ __launch_bounds__(T) void quantize_rows_loop(const float* __restrict__ x, int64_t ldx,
                                                         uint8_t* __restrict__ q, int64_t ldq,
-                                                        float* __restrict__ scales, int64_t rows, int64_t K4) {
+                                                        float* __restrict__ scales, int64_t rows, int64_t K4,
+                                                        const float* __restrict__ param) {
     __shared__ float red[T / kWave];
     for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
         const float4* xr = reinterpret_cast<const float4*>(x + r * ldx);
         float amax = 0.0f;
-        for (int64_t j = threadIdx.x; j < K4; j += T) amax = absmax4(amax, xr[j]);
-        amax = block_max<T>(amax, red);
-        const RowScale rs = make_row_scale(amax);
+        if constexpr (MODE != 1) {
+            for (int64_t j = threadIdx.x; j < K4; j += T) amax = absmax4(amax, xr[j]);
+            amax = block_max<T>(amax, red);
+        }
+        const RowScale rs = mode_scale<MODE>(amax, param);
         if (threadIdx.x == 0) scales[r] = rs.s;
         uint32_t* qr = reinterpret_cast<uint32_t*>(q + r * ldq);
         for (int64_t j = threadIdx.x; j < K4; j += T) qr[j] = cast4(xr[j], rs);
     }
 }
 
-template <int T>
+template <int T, int MODE>
 static void launch_rows(const float* x, int64_t ldx, uint8_t* q, int64_t ldq, float* scales, int64_t rows,
-                        int64_t K4, hipStream_t stream) {
+                        int64_t K4, const float* param, hipStream_t stream) {
     const dim3 grid((unsigned)(rows < (1 << 20) ? rows : (1 << 20))), block(T);
     const int k4 = (int)K4;
+#define FP8K_Q_REGS(V) \
+    hipLaunchKernelGGL((quantize_rows_regs<V, T, MODE>), grid, block, 0, stream, x, ldx, q, ldq, scales, rows, k4, param)
     if (K4 <= T * 1)
-        hipLaunchKernelGGL((quantize_rows_regs<1, T>), grid, block, 0, stream, x, ldx, q, ldq, scales, rows, k4);
+        FP8K_Q_REGS(1);
     else if (K4 <= T * 2)
-        hipLaunchKernelGGL((quantize_rows_regs<2, T>), grid, block, 0, stream, x, ldx, q, ldq, scales, rows, k4);
+        FP8K_Q_REGS(2);
     else if (K4 <= T * 4)
-        hipLaunchKernelGGL((quantize_rows_regs<4, T>), grid, block, 0, stream, x, ldx, q, ldq, scales, rows, k4);
+        FP8K_Q_REGS(4);
     else if (K4 <= T * 8)
-        hipLaunchKernelGGL((quantize_rows_regs<8, T>), grid, block, 0, stream, x, ldx, q, ldq, scales, rows, k4);
+        FP8K_Q_REGS(8);
     else if (K4 <= T * 16)
-        hipLaunchKernelGGL((quantize_rows_regs<16, T>), grid, block, 0, stream, x, ldx, q, ldq, scales, rows, k4);
+        FP8K_Q_REGS(16);
     else if (T == kQThreads && K4 <= T * 32)
-        hipLaunchKernelGGL((quantize_rows_regs<32, kQThreads>), grid, block, 0, stream, x, ldx, q, ldq, scales, rows,
-                           k4);
+        hipLaunchKernelGGL((quantize_rows_regs<32, kQThreads, MODE>), grid, block, 0, stream, x, ldx, q, ldq, scales,
+                           rows, k4, param);
     else
-        hipLaunchKernelGGL((quantize_rows_loop<T>), grid, block, 0, stream, x, ldx, q, ldq, scales, rows, K4);
+        hipLaunchKernelGGL((quantize_rows_loop<T, MODE>), grid, block, 0, stream, x, ldx, q, ldq, scales, rows, K4,
+                           param);
+#undef FP8K_Q_REGS
+}
+
+template <int MODE>
+static hipError_t launch_mode(const float* x, int64_t ldx, uint8_t* q, int64_t ldq, float* scales, int64_t rows,
+                              int64_t K, const float* param, hipStream_t stream) {
+    if (rows <= 0) return hipSuccess;
+    if (rows < kQWideRowsBelow)
+        launch_rows<kQThreadsWide, MODE>(x, ldx, q, ldq, scales, rows, K / 4, param, stream);
+    else
+        launch_rows<kQThreads, MODE>(x, ldx, q, ldq, scales, rows, K / 4, param, stream);
+    return hipGetLastError();
 }
 
 hipError_t launch_quantize_rows(const float* x, int64_t ldx, uint8_t* q, int64_t ldq, float* scales,
                                 int64_t rows, int64_t K, hipStream_t stream) {
-    if (rows <= 0) return hipSuccess;
-    if (rows < kQWideRowsBelow)
-        launch_rows<kQThreadsWide>(x, ldx, q, ldq, scales, rows, K / 4, stream);
-    else
-        launch_rows<kQThreads>(x, ldx, q, ldq, scales, rows, K / 4, stream);
-    return hipGetLastError();
+    return launch_mode<0>(x, ldx, q, ldq, scales, rows, K, nullptr, stream);
+}
+
+hipError_t launch_quantize_static(const float* x, int64_t ldx, const float* scale, uint8_t* q, int64_t ldq,
+                                  float* scales, int64_t rows, int64_t K, hipStream_t stream) {
+    return launch_mode<1>(x, ldx, q, ldq, scales, rows, K, scale, stream);
+}
+
+hipError_t launch_quantize_clipped(const float* x, int64_t ldx, const float* clip, uint8_t* q, int64_t ldq,
+                                   float* scales, int64_t rows, int64_t K, hipStream_t stream) {
+    return launch_mode<2>(x, ldx, q, ldq, scales, rows, K, clip, stream);
 }
 
 }  // namespace fp8k

@@ -85,6 +85,50 @@ fp8_status_t fp8_quantize_per_token(const float* x, int64_t rows, int64_t K, int
                                     hipStream_t stream);
 
 /*
+ * Static (calibrated, per-tensor) activation quantization (DeepSeek V4 950
+ * page, §3.1: the static part of the activation scale is computed offline
+ * from calibration data; §2.4: per-tensor scales):
+ *   s          = max(*scale, 1e-12f)          (scale: one fp32 on the device)
+ *   q[r,k]     = E4M3 code of fl32(x[r,k] / s), RNE, saturating +-448
+ *   scales_out[r] = s for every row (so the GEMM can take it as s_tok)
+ * Unlike the absmax scale, a static scale lets quotients exceed 448: they
+ * saturate (the clip of §4.2 of the same page).  No workspace.
+ */
+fp8_status_t fp8_quantize_static(const float* x, int64_t rows, int64_t K, int64_t ldx,
+                                 const float* scale, uint8_t* q, int64_t ldq, float* scales_out,
+                                 hipStream_t stream);
+
+/*
+ * Per-token quantization with a static clip (the hybrid per-token + per-tensor
+ * activation scale of the DeepSeek V4 950 page, §2.4 and §3.1; values above a
+ * calibrated percentile clipped, §4.2):
+ *   scales[r] = max(fl32(min(max_k |x[r,k]|, *clip) / 448), 1e-12f)
+ *   q[r,k]    = E4M3 code of fl32(x[r,k] / scales[r]), RNE, saturating +-448
+ * clip: one fp32 on the device (e.g. the P99.99 of |x| from
+ * fp8_calibrate_percentile).  No workspace.
+ */
+fp8_status_t fp8_quantize_per_token_clipped(const float* x, int64_t rows, int64_t K, int64_t ldx,
+                                            const float* clip, uint8_t* q, int64_t ldq, float* scales,
+                                            hipStream_t stream);
+
+/*
+ * Calibration percentile (DeepSeek V4 950 page, §3.1 step 1 and 3, §4.2):
+ * the nearest-rank percentile num/den of |x| over the n values of x (any
+ * layout, fp32, device): *value_out = the r-th smallest |x| with
+ * r = ceil(num * n / den) (clamped to [1, n]); scale_out (nullable) receives
+ * the static scale max(fl32(*value_out / 448), 1e-12f).  E.g. num/den =
+ * 999/1000 for P99.9.  0 < num <= den, 1 <= n <= 2^32 - 1.  ws: at least
+ * fp8_calibrate_workspace_bytes() bytes, 16-byte aligned.  The inputs are
+ * assumed finite.
+ */
+fp8_status_t fp8_calibrate_percentile(const float* x, int64_t n, int64_t num, int64_t den,
+                                      float* value_out, float* scale_out,
+                                      void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes fp8_calibrate_percentile needs (host only). */
+size_t fp8_calibrate_workspace_bytes(void);
+
+/*
  * Scaled FP8 GEMM with BF16 output (DeepSeek V4 950 page, §2.3 FP8 inputs
  * with FP32 accumulation; §2.4 per-token x per-channel scales):
  *   y[m,n] = bf16_rne( (sum_k e4m3(qa[m,k]) * e4m3(qw[n,k])) * (s_tok[m] * s_ch[n]) )
@@ -108,8 +152,8 @@ fp8_status_t fp8_gemm_scaled(const uint8_t* qa, int64_t lda, const float* s_tok,
  * when given they receive the activation codes and scales.  ws must hold at
  * least fp8_workspace_bytes(M, N, K) bytes.
  * For M <= 16 rows with M * (K + 16) <= 65792 and ceil(K / 256) <= 16
- * (M <= 8) or <= 8 (M <= 16), and N > 0, the call runs as one kernel that
- * quantizes x in each workgroup's prologue (ws is then not touched); the
+ * (M <= 8) or <= 8 (M <= 16), and 0 < N <= 8192, the call runs as one kernel
+ * that quantizes x in each workgroup's prologue (ws is then not touched); the
  * codes, scales and y are the same bytes either way.
  */
 fp8_status_t fp8_quant_gemm_fused(const float* x, int64_t ldx, const uint8_t* qw, int64_t ldw,

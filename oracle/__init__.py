@@ -45,6 +45,10 @@ def lib():
         L.oracle_e4m3_encode_array.argtypes = [vp, i64, vp]
         L.oracle_quantize_rows.restype = None
         L.oracle_quantize_rows.argtypes = [vp, i64, i64, i64, vp, i64, vp]
+        L.oracle_quantize_static.restype = None
+        L.oracle_quantize_static.argtypes = [vp, i64, i64, i64, ctypes.c_float, vp, i64]
+        L.oracle_quantize_rows_clipped.restype = None
+        L.oracle_quantize_rows_clipped.argtypes = [vp, i64, i64, i64, ctypes.c_float, vp, i64, vp]
         L.oracle_gemm_ref.restype = None
         L.oracle_gemm_ref.argtypes = [vp, i64, vp, vp, i64, vp, i64, i64, i64, vp, vp]
         L.oracle_gemm_ref_sampled.restype = None
@@ -102,6 +106,42 @@ def quantize_rows(x):
     s = np.empty(rows, dtype=np.float32)
     lib().oracle_quantize_rows(_p(x), rows, K, K, _p(q), K, _p(s))
     return q, s
+
+
+def quantize_static(x, scale):
+    """Static per-tensor quantization of a 2-D float32 array with one scale
+    (saturating) -> codes uint8.  The scale is used as given."""
+    x = _c(x, np.float32)
+    rows, K = x.shape
+    q = np.empty((rows, K), dtype=np.uint8)
+    lib().oracle_quantize_static(_p(x), rows, K, K, np.float32(scale), _p(q), K)
+    return q
+
+
+def quantize_rows_clipped(x, clip):
+    """Per-row absmax quantization with the absmax clipped at `clip` -> (codes, scales)."""
+    x = _c(x, np.float32)
+    rows, K = x.shape
+    q = np.empty((rows, K), dtype=np.uint8)
+    s = np.empty(rows, dtype=np.float32)
+    lib().oracle_quantize_rows_clipped(_p(x), rows, K, K, np.float32(clip), _p(q), K, _p(s))
+    return q, s
+
+
+def percentile_nearest_rank(x, num, den):
+    """Nearest-rank percentile num/den of |x| (DeepSeek V4 950 page, §3.1): the
+    r-th smallest |x| with r = ceil(num * n / den), clamped to [1, n]."""
+    a = np.sort(np.abs(np.asarray(x, dtype=np.float32)).ravel())
+    n = a.size
+    r = -(-(int(num) * n) // int(den))
+    r = min(max(r, 1), n)
+    return np.float32(a[r - 1])
+
+
+def static_scale(value):
+    """The static scale of a calibrated magnitude: max(fl32(value / 448), 1e-12f)."""
+    s = np.float32(value) / np.float32(E4M3_MAX)
+    return np.float32(max(s, SCALE_FLOOR))
 
 
 def gemm_ref(qa, s_tok, qw, s_ch):

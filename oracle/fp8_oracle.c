@@ -124,6 +124,42 @@ void oracle_quantize_rows(const float* x, int64_t rows, int64_t K, int64_t ldx,
     }
 }
 
+/* Static (calibrated, per-tensor) quantization: one scale s for the whole
+ * tensor, computed offline from a percentile of |x| over calibration data
+ * ([DSV4] §3.1: P99.9 of the activation magnitudes instead of the maximum;
+ * §4.2: values beyond the range clipped).  Quotients above 448 saturate, the
+ * clamp of [FP8DEP] §2.3:
+ *   q[r,k] = enc(fl32(x[r,k] / s))                                          */
+void oracle_quantize_static(const float* x, int64_t rows, int64_t K, int64_t ldx, float s,
+                            uint8_t* q, int64_t ldq) {
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t k = 0; k < K; ++k) q[r * ldq + k] = oracle_e4m3_encode(x[r * ldx + k] / s);
+}
+
+/* Per-token quantization with a static clip (the per-token + per-tensor
+ * hybrid of [DSV4] §2.4; outliers above a calibrated percentile clipped,
+ * §4.2):
+ *   scale[r] = max(fl32(min(max_k |x[r,k]|, clip) / 448), 1e-12f)
+ *   q[r,k]   = enc(fl32(x[r,k] / scale[r]))                                 */
+void oracle_quantize_rows_clipped(const float* x, int64_t rows, int64_t K, int64_t ldx, float clip,
+                                  uint8_t* q, int64_t ldq, float* scales) {
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t r = 0; r < rows; ++r) {
+        const float* xr = x + r * ldx;
+        float amax = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            float a = fabsf(xr[k]);
+            if (a > amax) amax = a;
+        }
+        if (clip < amax) amax = clip;
+        float s = amax / 448.0f;
+        if (s < 1e-12f) s = 1e-12f;
+        scales[r] = s;
+        for (int64_t k = 0; k < K; ++k) q[r * ldq + k] = oracle_e4m3_encode(xr[k] / s);
+    }
+}
+
 /* --------------------------------------------------------------- GEMM ---- */
 
 static double g_dec[256];

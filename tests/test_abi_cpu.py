@@ -212,3 +212,25 @@ def test_python_binding_requires_cuda_tensors(name):
         else:
             fn(torch.zeros(2, 16, dtype=torch.uint8), torch.ones(2), torch.zeros(2, dtype=torch.int32),
                torch.zeros(2, dtype=torch.int32), torch.zeros(1, 2, 16, dtype=torch.uint8), torch.ones(1, 2))
+
+
+def test_static_clipped_and_calibration_validation():
+    L = fp8.lib()
+    # x, rows, K, ldx, scale, q, ldq, scales_out, stream
+    assert L.fp8_quantize_static(P, 4, 15, 16, P, Q, 16, P, S0) == FP8_ERR_UNSUPPORTED       # K % 16
+    assert L.fp8_quantize_static(P, 4, 16, 16, 0, Q, 16, P, S0) == FP8_ERR_INVALID_ARGUMENT  # no scale
+    assert L.fp8_quantize_static(P, 4, 16, 16, P + 2, Q, 16, P, S0) == FP8_ERR_UNSUPPORTED   # misaligned scale
+    assert L.fp8_quantize_static(P, 4, 16, 16, P, Q, 16, 0, S0) == FP8_ERR_INVALID_ARGUMENT  # no scales_out
+    assert L.fp8_quantize_static(0, 0, 16, 16, 0, 0, 16, 0, S0) == FP8_OK                    # empty
+    assert L.fp8_quantize_per_token_clipped(P, 4, 16, 16, 0, Q, 16, P, S0) == FP8_ERR_INVALID_ARGUMENT
+    assert L.fp8_quantize_per_token_clipped(P, 4, 16, 12, P, Q, 16, P, S0) == FP8_ERR_INVALID_ARGUMENT
+    # x, n, num, den, value_out, scale_out, ws, ws_bytes, stream
+    wsb = L.fp8_calibrate_workspace_bytes()
+    assert wsb >= 1040
+    assert L.fp8_calibrate_percentile(P, 0, 999, 1000, P, P, Q, wsb, S0) == FP8_ERR_INVALID_ARGUMENT
+    assert L.fp8_calibrate_percentile(P, 10, 0, 1000, P, P, Q, wsb, S0) == FP8_ERR_INVALID_ARGUMENT
+    assert L.fp8_calibrate_percentile(P, 10, 1001, 1000, P, P, Q, wsb, S0) == FP8_ERR_INVALID_ARGUMENT
+    assert L.fp8_calibrate_percentile(P, 10, 999, 1000, P, P, Q, wsb - 1, S0) == FP8_ERR_WORKSPACE
+    assert L.fp8_calibrate_percentile(P, 10, 999, 1000, P, P, MIS, wsb, S0) == FP8_ERR_UNSUPPORTED
+    assert L.fp8_calibrate_percentile(P, 1 << 33, 999, 1000, P, P, Q, wsb, S0) == FP8_ERR_UNSUPPORTED
+    assert L.fp8_calibrate_percentile(0, 10, 999, 1000, P, P, Q, wsb, S0) == FP8_ERR_INVALID_ARGUMENT

@@ -145,10 +145,11 @@ def test_split_k_strided_output_and_stale_workspace():
     assert np.array_equal(y2, yh[:, :N])
 
 
-# M <= 16 rows whose codes fit in LDS take the one-kernel path (rows up to
-# 4096 held in registers, longer rows read twice); the rest quantize first.
+# M <= 16 rows whose codes fit in LDS and whose fp32 values fit in registers
+# (K <= 4096 for M <= 8, K <= 2048 for M <= 16), with N <= 8192, take the
+# one-kernel path; the rest quantize first.
 FUSED_SHAPES = [(1, 16, 16), (8, 512, 1024), (5, 4096 + 48, 272), (16, 300, 4096), (12, 3000, 4112),
-                (8, 1000, 8192), (16, 100, 4112), (17, 300, 640), (200, 300, 640)]
+                (8, 1000, 8192), (16, 100, 4112), (8, 8192 + 16, 1024), (17, 300, 640), (200, 300, 640)]
 
 
 @pytest.mark.parametrize("M,N,K", FUSED_SHAPES)
