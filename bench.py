@@ -213,6 +213,8 @@ def main():
             print("--out fp8 is for the dense workloads", file=sys.stderr)
             sys.exit(2)
         return bench_fp8out(args, w, dev, steps, warmup, graph, log)
+    if w["kind"] == "kv":
+        return bench_kv(args, w, dev, steps, warmup, graph, log)
     if w["kind"] == "dense":
         M, N, K = w["M"], w["N"], w["K"]
         log(f"[bench] {args.workload}: generating inputs M={M} N={N} K={K}")
@@ -450,6 +452,108 @@ def bench_fp8out(args, w, dev, steps, warmup, graph, log):
         "config": cfg, "roofline": roof, "cpu_baseline": None, "detail": extra,
     }
     print(json.dumps(out), flush=True)
+
+
+def bench_kv(args, w, dev, steps, warmup, graph, log):
+    """One step = writing one layer's prefill KV into the paged FP8 cache:
+    fp8_kv_channel_scales (per-channel scales of the batch) then
+    fp8_kv_quantize_paged (codes into the slots the block table names).  The
+    read back (fp8_kv_dequantize_paged, what attention would consume) is timed
+    on its own.  Two copies of the batch are rotated so the 256 MB Infinity
+    Cache cannot carry a step's input into the next step."""
+    import numpy as np
+    import torch
+    import fp8_w8a8_quantized_quantize_amd as fp8
+    import synth
+    T, C, B, fmt = w["T"], w["C"], w["block"], w["fmt"]
+    nb = T // B + 256
+    log(f"[bench] {args.workload}: generating inputs T={T} C={C} block={B} blocks={nb} fmt={fmt}")
+    kv = synth.kv_activations(T, C, seed=args.seed)
+    slot = synth.kv_slot_mapping(T, B, nb, seed=args.seed)
+    copies = 2
+    kvd = [torch.from_numpy(kv).to(dev)]
+    kvd += [kvd[0].clone() for _ in range(copies - 1)]
+    slotd = torch.from_numpy(slot).to(dev)
+    cache = torch.zeros((nb * B, C), dtype=torch.uint8, device=dev)
+    scales = torch.empty(C, dtype=torch.float32, device=dev)
+    ws = torch.empty(fp8.fp8_kv_scales_workspace_bytes(T, C), dtype=torch.uint8, device=dev)
+    out = torch.empty((T, C), dtype=torch.float32, device=dev)
+
+    def step(i):
+        fp8.fp8_kv_channel_scales(kvd[i % copies], fmt, scales=scales, ws=ws)
+        fp8.fp8_kv_quantize_paged(kvd[i % copies], scales, slotd, cache, fmt)
+
+    def scales_only(i):
+        fp8.fp8_kv_channel_scales(kvd[i % copies], fmt, scales=scales, ws=ws)
+
+    def quant_only(i):
+        fp8.fp8_kv_quantize_paged(kvd[i % copies], scales, slotd, cache, fmt)
+
+    def read_back(i):
+        fp8.fp8_kv_dequantize_paged(cache, slotd, scales, fmt, out=out)
+
+    log(f"[bench] warmup {warmup}, timing {steps} steps")
+    total_ms, per = time_loop(step, steps, warmup, graph)
+    sc_ms, _ = time_loop(scales_only, steps, warmup, graph)
+    q_ms, _ = time_loop(quant_only, steps, warmup, graph)
+    dq_ms, _ = time_loop(read_back, steps, warmup, graph)
+    ms, sc_ms, q_ms, dq_ms = total_ms / steps, sc_ms / steps, q_ms / steps, dq_ms / steps
+    # algorithmic bytes: the batch read once, codes written once, scales and slots
+    step_bytes = 4 * T * C + T * C + 4 * C + 4 * T
+    scale_bytes = 4 * T * C + 4 * C
+    quant_bytes = 4 * T * C + 4 * C + 4 * T + T * C
+    dq_bytes = T * C + 4 * T + 4 * C + 4 * T * C
+    gbs = lambda b, t: b / (t * 1e-3) / 1e9
+    value = gbs(step_bytes, ms)
+    q_ach = gbs(quant_bytes, q_ms)
+    roof = dict(bound="hbm", achieved=round(q_ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=round(q_ach / HBM_PEAK_GBS, 4), kernel="kv_quantize_paged",
+                per_launch=f"{quant_bytes} algorithmic bytes (fp32 kv in, slots, scales, FP8 codes out)",
+                avg_launch_us=round(q_ms * 1e3, 3), traffic=None,
+                others=dict(channel_scales=dict(kernels="kv_amax_partial + kv_scale_finish",
+                                                avg_us=round(sc_ms * 1e3, 3), achieved=round(gbs(scale_bytes, sc_ms), 1),
+                                                frac=round(gbs(scale_bytes, sc_ms) / HBM_PEAK_GBS, 4),
+                                                per_launch=f"{scale_bytes} algorithmic bytes"),
+                            read_back=dict(kernel="kv_dequantize_paged", avg_us=round(dq_ms * 1e3, 3),
+                                           achieved=round(gbs(dq_bytes, dq_ms), 1),
+                                           frac=round(gbs(dq_bytes, dq_ms) / HBM_PEAK_GBS, 4),
+                                           per_launch=f"{dq_bytes} algorithmic bytes")))
+    cfg = dict(workload=args.workload, T=T, C=C, block=B, blocks=nb, fmt=fmt, seed=args.seed, kv_copies=copies,
+               step="fp8_kv_channel_scales + fp8_kv_quantize_paged")
+    extra = dict(timing="hip-graph replay of the steps" if graph else "eager launches", step_us=round(ms * 1e3, 3),
+                 step_gbs_counting_both_reads=round(gbs(step_bytes + 4 * T * C, ms), 1))
+    if per:
+        extra.update(step_us_median=round(pct(per, 0.5) * 1e3, 3))
+    cpu = None
+    if not args.no_cpu_baseline and not args.profile:
+        import oracle
+        log("[bench] timing the CPU oracle")
+        rows = min(T, 4096)
+        fid = oracle.E5M2 if fmt == "e5m2" else oracle.E4M3
+        # the sample's slots, renumbered into a cache of `rows` rows (same scatter order)
+        compact = np.empty(rows, dtype=np.int32)
+        compact[np.argsort(slot[:rows], kind="stable")] = np.arange(rows, dtype=np.int32)
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            s_h = oracle.kv_channel_scales(kv[:rows], fid)
+            oracle.kv_quantize(kv[:rows], s_h, fid, compact, rows)
+            reps += 1
+            elapsed = time.perf_counter() - t0
+            if elapsed >= args.cpu_seconds:
+                break
+        b = reps * (4 * rows * C + rows * C + 4 * C + 4 * rows)
+        cpu = dict(value=round(b / elapsed / 1e9, 6), unit="GB/s", cores=oracle.num_threads(), kind="oracle",
+                   seconds=round(elapsed, 2),
+                   sample=f"{reps} pass(es) of channel scales + paged quantize over the first {rows} of {T} tokens "
+                          f"(their slots renumbered into a {rows}-row cache)")
+    res = {
+        "metric": METRIC, "value": round(value, 3), "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": f"fp32 in, {fmt} codes", "data": "synthetic (seeded; no dataset, no trained weights)",
+        "config": cfg, "roofline": roof, "cpu_baseline": cpu, "detail": extra,
+    }
+    print(json.dumps(res), flush=True)
 
 
 if __name__ == "__main__":

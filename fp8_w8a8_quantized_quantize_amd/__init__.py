@@ -34,7 +34,8 @@ FP8_ERR_DEVICE = 4
 EXPORTS = ("fp8_quantize_per_token", "fp8_quantize_static", "fp8_quantize_per_token_clipped",
            "fp8_calibrate_percentile", "fp8_calibrate_workspace_bytes", "fp8_gemm_scaled", "fp8_quant_gemm_fused", "fp8_gemm_scaled_fp8out",
            "fp8_gemm_grouped_scaled", "fp8_workspace_bytes", "fp8_fp8out_workspace_bytes",
-           "fp8_grouped_workspace_bytes", "fp8_status_string")
+           "fp8_grouped_workspace_bytes", "fp8_kv_channel_scales", "fp8_kv_scales_workspace_bytes",
+           "fp8_kv_quantize_paged", "fp8_kv_dequantize_paged", "fp8_status_string")
 
 _lib = None
 
@@ -78,6 +79,14 @@ def lib():
         L.fp8_workspace_bytes.argtypes = [i64, i64, i64]
         L.fp8_grouped_workspace_bytes.restype = sz
         L.fp8_grouped_workspace_bytes.argtypes = [i64, i64, i64, i64, i64]
+        L.fp8_kv_channel_scales.restype = st
+        L.fp8_kv_channel_scales.argtypes = [vp, i64, i64, i64, st, vp, vp, sz, vp]
+        L.fp8_kv_scales_workspace_bytes.restype = sz
+        L.fp8_kv_scales_workspace_bytes.argtypes = [i64, i64]
+        L.fp8_kv_quantize_paged.restype = st
+        L.fp8_kv_quantize_paged.argtypes = [vp, i64, i64, i64, vp, st, vp, vp, i64, vp]
+        L.fp8_kv_dequantize_paged.restype = st
+        L.fp8_kv_dequantize_paged.argtypes = [vp, i64, vp, i64, i64, vp, st, vp, i64, vp]
         L.fp8_status_string.restype = ctypes.c_char_p
         L.fp8_status_string.argtypes = [st]
         _lib = L
@@ -209,6 +218,77 @@ def fp8_calibrate_percentile(x, num, den, stream=None):
            lib().fp8_calibrate_percentile(_ptr(x), x.numel(), int(num), int(den), _ptr(value), _ptr(scale), _ptr(ws),
                                           ws.numel(), _stream(stream)))
     return value, scale
+
+
+FP8_KV_E4M3 = 0
+FP8_KV_E5M2 = 1
+_KV_FORMATS = {"e4m3": FP8_KV_E4M3, "e5m2": FP8_KV_E5M2, FP8_KV_E4M3: FP8_KV_E4M3, FP8_KV_E5M2: FP8_KV_E5M2}
+
+
+def _kv_fmt(fmt):
+    if fmt not in _KV_FORMATS:
+        raise ValueError(f"fmt: expected 'e4m3' or 'e5m2', got {fmt!r}")
+    return _KV_FORMATS[fmt]
+
+
+def fp8_kv_scales_workspace_bytes(T, C):
+    return int(lib().fp8_kv_scales_workspace_bytes(T, C))
+
+
+def fp8_kv_channel_scales(kv, fmt="e5m2", scales=None, ws=None, stream=None):
+    """Per-channel scales max(fl32(max_t |kv[t,c]| / fmt_max), 1e-12f) of fp32
+    kv [T, C] -> scales fp32 [C]."""
+    torch = _torch()
+    T, C, ldkv = _rows(kv, torch.float32, "kv")
+    if scales is None:
+        scales = torch.empty(C, dtype=torch.float32, device=kv.device)
+    _vec(scales, torch.float32, "scales", C)
+    if ws is None:
+        need = fp8_kv_scales_workspace_bytes(T, C)
+        if need == (1 << 64) - 1:
+            raise Fp8Error("fp8_kv_channel_scales", 2)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=kv.device)
+    _check("fp8_kv_channel_scales",
+           lib().fp8_kv_channel_scales(_ptr(kv), T, C, ldkv, _kv_fmt(fmt), _ptr(scales), _ptr(ws),
+                                       ws.numel() * ws.element_size(), _stream(stream)))
+    return scales
+
+
+def fp8_kv_quantize_paged(kv, scales, slot_mapping, cache, fmt="e5m2", stream=None):
+    """Write fp32 kv [T, C] into the rows slot_mapping[t] of the uint8 cache
+    [num_slots, C] (contiguous) as FP8 codes of kv / scales; returns cache."""
+    torch = _torch()
+    T, C, ldkv = _rows(kv, torch.float32, "kv")
+    _vec(scales, torch.float32, "scales", C)
+    _vec(slot_mapping, torch.int32, "slot_mapping", T)
+    if not isinstance(cache, torch.Tensor) or cache.dtype != torch.uint8 or not cache.is_cuda \
+            or not cache.is_contiguous() or cache.dim() != 2 or cache.shape[1] != C:
+        raise TypeError("cache: expected a contiguous uint8 CUDA tensor [num_slots, C]")
+    _check("fp8_kv_quantize_paged",
+           lib().fp8_kv_quantize_paged(_ptr(kv), T, C, ldkv, _ptr(scales), _kv_fmt(fmt), _ptr(slot_mapping),
+                                       _ptr(cache), cache.shape[0], _stream(stream)))
+    return cache
+
+
+def fp8_kv_dequantize_paged(cache, slot_mapping, scales, fmt="e5m2", out=None, stream=None):
+    """Read cache rows slot_mapping[t] back -> fp32 out [T, C]."""
+    torch = _torch()
+    if not isinstance(cache, torch.Tensor) or cache.dtype != torch.uint8 or not cache.is_cuda \
+            or not cache.is_contiguous() or cache.dim() != 2:
+        raise TypeError("cache: expected a contiguous uint8 CUDA tensor [num_slots, C]")
+    num_slots, C = cache.shape
+    T = slot_mapping.numel()
+    _vec(slot_mapping, torch.int32, "slot_mapping", T)
+    _vec(scales, torch.float32, "scales", C)
+    if out is None:
+        out = torch.empty((T, C), dtype=torch.float32, device=cache.device)
+    T2, C2, ldo = _rows(out, torch.float32, "out")
+    if (T2, C2) != (T, C):
+        raise ValueError("out: expected shape [T, C]")
+    _check("fp8_kv_dequantize_paged",
+           lib().fp8_kv_dequantize_paged(_ptr(cache), num_slots, _ptr(slot_mapping), T, C, _ptr(scales),
+                                         _kv_fmt(fmt), _ptr(out), ldo, _stream(stream)))
+    return out
 
 
 def fp8_gemm_scaled(qa, s_tok, qw, s_ch, y=None, ws=None, stream=None):

@@ -97,10 +97,14 @@ __device__ __forceinline__ RowScale make_row_scale(float amax) {
 // reciprocal and two FMAs instead of a full IEEE division per element).  The
 // sign of x is put back so -0 stays -0.  Where x is subnormal the residual
 // can lose bits, but the quotient is then below 2^-11, whose E4M3 code is the
-// signed zero either way.  A CPU test checks this against IEEE division on
-// random and on E4M3-boundary quotients.
+// signed zero either way (E5M2's smallest step is 2^-16, so there too).
+// q0 is clamped to +-2^20: when x * r overflows fp32 (a static or stale
+// scale far below |x| / 448) the residual would otherwise be inf - inf; a
+// clamped quotient is past every FP8 code and still saturates.  A CPU test
+// checks all of this against IEEE division on random, overflowing and
+// FP8-boundary quotients.
 __device__ __forceinline__ float div_by_scale(float x, const RowScale& rs) {
-    const float q0 = x * rs.r;
+    const float q0 = __builtin_amdgcn_fmed3f(x * rs.r, -1048576.0f, 1048576.0f);
     const float e = __builtin_fmaf(-q0, rs.s, x);
     return __builtin_copysignf(__builtin_fmaf(e, rs.r, q0), x);
 }

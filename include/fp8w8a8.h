@@ -219,6 +219,63 @@ size_t fp8_workspace_bytes(int64_t M, int64_t N, int64_t K);
 /* Workspace bytes fp8_gemm_grouped_scaled needs (host-only, pure). */
 size_t fp8_grouped_workspace_bytes(int64_t T, int64_t R, int64_t E, int64_t N, int64_t K);
 
+/*
+ * FP8 KV cache (DeepSeek V4 950 page, §2.1: E5M2 for the KV cache, §2.2:
+ * one scale per latent dimension, paged blocks; 512K-context page, §3.3:
+ * block pool with per-request block tables, per-channel FP8 scales; FP8
+ * deployment page, §2.3: the E4M3 KV variant and its absmax/448 scale).
+ *
+ * A KV batch is T token rows of C channels (e.g. the K and V heads of one
+ * layer side by side, or one latent vector): kv fp32 [T, C], row stride
+ * ldkv.  The cache is a pool of num_slots rows of C codes (u8 [num_slots, C],
+ * unit-stride rows of exactly C bytes); slot_mapping int32 [T] names each
+ * token's row, physical block * block size + offset in the block, as the
+ * caller's block table resolves it.  fmt picks the code format; scales are
+ * fp32 [C], one per channel, floored at 1e-12f wherever they are used.
+ * C must be a multiple of 4; kv and out row strides multiples of 4
+ * elements; kv, scales, cache, out 16-byte aligned (else
+ * FP8_ERR_UNSUPPORTED).  T, C, num_slots <= 2^31 - 1.  Inputs are assumed
+ * finite.
+ */
+typedef enum { FP8_KV_E4M3 = 0, FP8_KV_E5M2 = 1 } fp8_kv_format_t;
+
+/*
+ * Per-channel scales of a KV batch (the online calibration of the Llama 3
+ * FP8 page, §3.2, per channel):
+ *   scales[c] = max(fl32(max_t |kv[t,c]| / fmt_max), 1e-12f),
+ * fmt_max = 448 (E4M3) or 57344 (E5M2).  T == 0 gives the floor.  ws: at
+ * least fp8_kv_scales_workspace_bytes(T, C) bytes, 16-byte aligned.
+ */
+fp8_status_t fp8_kv_channel_scales(const float* kv, int64_t T, int64_t C, int64_t ldkv, fp8_kv_format_t fmt,
+                                   float* scales, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes fp8_kv_channel_scales needs (host only; SIZE_MAX for
+ * invalid sizes). */
+size_t fp8_kv_scales_workspace_bytes(int64_t T, int64_t C);
+
+/*
+ * Quantize a KV batch into its cache slots:
+ *   cache[slot_mapping[t], c] = enc_fmt(fl32(kv[t,c] / scales[c]))
+ * rounded to nearest even and saturating at the format's largest finite
+ * value (+-448 or +-57344).  Tokens whose slot is outside [0, num_slots)
+ * (padding carries -1) are skipped; cache rows no token names are left
+ * as they were.  Two tokens naming the same slot race (one of them wins).
+ * No workspace.
+ */
+fp8_status_t fp8_kv_quantize_paged(const float* kv, int64_t T, int64_t C, int64_t ldkv, const float* scales,
+                                   fp8_kv_format_t fmt, const int32_t* slot_mapping, uint8_t* cache,
+                                   int64_t num_slots, hipStream_t stream);
+
+/*
+ * Read a sequence's rows back out of the cache:
+ *   out[t,c] = fl32(dec_fmt(cache[slot_mapping[t], c]) * scales[c])
+ * out fp32 [T, C], row stride ldo; a slot outside [0, num_slots) gives a
+ * row of +0.  No workspace.
+ */
+fp8_status_t fp8_kv_dequantize_paged(const uint8_t* cache, int64_t num_slots, const int32_t* slot_mapping,
+                                     int64_t T, int64_t C, const float* scales, fp8_kv_format_t fmt, float* out,
+                                     int64_t ldo, hipStream_t stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* fp8_status_string(fp8_status_t status);
 

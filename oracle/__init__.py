@@ -49,6 +49,18 @@ def lib():
         L.oracle_quantize_static.argtypes = [vp, i64, i64, i64, ctypes.c_float, vp, i64]
         L.oracle_quantize_rows_clipped.restype = None
         L.oracle_quantize_rows_clipped.argtypes = [vp, i64, i64, i64, ctypes.c_float, vp, i64, vp]
+        L.oracle_e5m2_decode.restype = ctypes.c_double
+        L.oracle_e5m2_decode.argtypes = [ctypes.c_uint8]
+        L.oracle_e5m2_encode.restype = ctypes.c_uint8
+        L.oracle_e5m2_encode.argtypes = [ctypes.c_float]
+        L.oracle_e5m2_encode_array.restype = None
+        L.oracle_e5m2_encode_array.argtypes = [vp, i64, vp]
+        L.oracle_kv_channel_scales.restype = None
+        L.oracle_kv_channel_scales.argtypes = [vp, i64, i64, i64, ctypes.c_int, vp]
+        L.oracle_kv_quantize.restype = None
+        L.oracle_kv_quantize.argtypes = [vp, i64, i64, i64, vp, ctypes.c_int, vp, vp, i64]
+        L.oracle_kv_dequantize.restype = None
+        L.oracle_kv_dequantize.argtypes = [vp, i64, vp, i64, i64, vp, ctypes.c_int, vp]
         L.oracle_gemm_ref.restype = None
         L.oracle_gemm_ref.argtypes = [vp, i64, vp, vp, i64, vp, i64, i64, i64, vp, vp]
         L.oracle_gemm_ref_sampled.restype = None
@@ -106,6 +118,64 @@ def quantize_rows(x):
     s = np.empty(rows, dtype=np.float32)
     lib().oracle_quantize_rows(_p(x), rows, K, K, _p(q), K, _p(s))
     return q, s
+
+
+E5M2 = 1
+E4M3 = 0
+
+
+def e5m2_decode(codes):
+    """E5M2 codes (uint8 array) -> float64 values (+-inf, NaN for the specials)."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    table = np.array([lib().oracle_e5m2_decode(c) for c in range(256)], dtype=np.float64)
+    return table[codes]
+
+
+def e5m2_encode(values):
+    """float32 array -> E5M2 codes (RNE, saturating to +-57344)."""
+    v = _c(values, np.float32)
+    out = np.empty(v.shape, dtype=np.uint8)
+    lib().oracle_e5m2_encode_array(_p(v), v.size, _p(out))
+    return out
+
+
+def e5m2_encode_fn_address():
+    return ctypes.cast(lib().oracle_e5m2_encode, ctypes.c_void_p).value
+
+
+def kv_channel_scales(kv, fmt):
+    """Per-channel KV scales of a [T, C] float32 batch: max(fl32(amax_c / fmt_max), 1e-12f)."""
+    kv = _c(kv, np.float32)
+    T, C = kv.shape
+    s = np.empty(C, dtype=np.float32)
+    lib().oracle_kv_channel_scales(_p(kv), T, C, C, int(fmt), _p(s))
+    return s
+
+
+def kv_quantize(kv, scales, fmt, slot, num_slots, cache=None):
+    """Quantize [T, C] KV into a paged cache uint8 [num_slots, C].  Tokens whose
+    slot is outside [0, num_slots) are skipped; rows no token maps to keep the
+    contents of `cache` (zeros when it is not given)."""
+    kv = _c(kv, np.float32)
+    T, C = kv.shape
+    cache = np.zeros((num_slots, C), dtype=np.uint8) if cache is None else _c(cache, np.uint8).copy()
+    assert cache.shape == (num_slots, C)
+    slot = _c(slot, np.int32)
+    assert slot.size == T
+    lib().oracle_kv_quantize(_p(kv), T, C, C, _p(_c(scales, np.float32)), int(fmt), _p(slot), _p(cache), num_slots)
+    return cache
+
+
+def kv_dequantize(cache, slot, scales, fmt):
+    """[T, C] float32 read back of the cache rows slot[t] (zeros for a slot
+    outside the cache)."""
+    cache = _c(cache, np.uint8)
+    slot = _c(slot, np.int32)
+    num_slots, C = cache.shape
+    out = np.empty((slot.size, C), dtype=np.float32)
+    lib().oracle_kv_dequantize(_p(cache), num_slots, _p(slot), slot.size, C, _p(_c(scales, np.float32)), int(fmt),
+                               _p(out))
+    return out
 
 
 def quantize_static(x, scale):

@@ -17,7 +17,10 @@
  *           clamped below at 1e-12, cast to float8_e4m3fn),
  *           §4.1 (scan quantized tensors for NaN/Inf).
  *   [DEPLOY] "FP8 mixed-precision inference deployment" (ybb.press),
- *           §1.1 (E4M3 range +-448), §2.3 (clamp to +-448).
+ *           §1.1 (E4M3 range +-448, E5M2 range +-57344), §2.3 (clamp to
+ *           +-448; the KV-cache scale sketch).
+ *   [SP512K] "512K context on 8 x H20" (hotelren.com), §3.3 (paged KV cache
+ *           in FP8 with per-channel scales).
  *
  * Readings where the pages leave a step open (all float arithmetic below is
  * IEEE binary32/binary64 with round-to-nearest-even; build without
@@ -97,6 +100,52 @@ void oracle_e4m3_encode_array(const float* v, int64_t n, uint8_t* out) {
     for (int64_t i = 0; i < n; ++i) out[i] = oracle_e4m3_encode(v[i]);
 }
 
+/* Value of an E5M2 code ([DSV4] §2.1: 5 exponent bits, 2 mantissa bits,
+ * range +-57344; [DEPLOY] §1.1): exponent field E (bias 15), mantissa m.
+ * E = 31 holds infinity (m = 0) and NaN (m != 0); E = 0 is subnormal
+ * m * 2^-16. */
+double oracle_e5m2_decode(uint8_t code) {
+    int s = (code >> 7) & 1;
+    int E = (code >> 2) & 31;
+    int m = code & 3;
+    double mag;
+    if (E == 31) return m ? NAN : (s ? -INFINITY : INFINITY);
+    if (E == 0)
+        mag = ldexp((double)m, -16);
+    else
+        mag = ldexp(1.0 + (double)m / 4.0, E - 15);
+    return s ? -mag : mag;
+}
+
+/* fp32 -> E5M2 code: round to nearest even on the E5M2 grid, saturate to
+ * +-57344 (the KV cache keeps finite values; the same clamp as for E4M3),
+ * NaN -> S.11111.11. */
+uint8_t oracle_e5m2_encode(float v) {
+    uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    if (isnan(v)) return (uint8_t)(sign | 0x7F);
+    double a = fabs((double)v);
+    if (a >= 57344.0) return (uint8_t)(sign | 0x7B);
+    if (a == 0.0) return sign;
+    int e2;
+    frexp(a, &e2);
+    int ex = e2 - 1;
+    if (ex < -14) {
+        /* below the smallest normal 2^-14: grid step 2^-16, codes 0..4 */
+        double r = round_half_even(ldexp(a, 16));
+        return (uint8_t)(sign | (int)r);
+    }
+    /* binade [2^ex, 2^(ex+1)): 4 steps of 2^(ex-2) */
+    double r = round_half_even(ldexp(a, 2 - ex)); /* in [4, 8] */
+    if (r == 8.0) { ex += 1; r = 4.0; }
+    int E = ex + 15, m = (int)r - 4;
+    return (uint8_t)(sign | (E << 2) | m);
+}
+
+void oracle_e5m2_encode_array(const float* v, int64_t n, uint8_t* out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_e5m2_encode(v[i]);
+}
+
 /* ------------------------------------------------------------ quantizer -- */
 
 /* Per-row absmax quantization, the [L3] §3.1 conversion applied to any
@@ -128,7 +177,7 @@ void oracle_quantize_rows(const float* x, int64_t rows, int64_t K, int64_t ldx,
  * tensor, computed offline from a percentile of |x| over calibration data
  * ([DSV4] §3.1: P99.9 of the activation magnitudes instead of the maximum;
  * §4.2: values beyond the range clipped).  Quotients above 448 saturate, the
- * clamp of [FP8DEP] §2.3:
+ * clamp of [DEPLOY] §2.3:
  *   q[r,k] = enc(fl32(x[r,k] / s))                                          */
 void oracle_quantize_static(const float* x, int64_t rows, int64_t K, int64_t ldx, float s,
                             uint8_t* q, int64_t ldq) {
@@ -158,6 +207,64 @@ void oracle_quantize_rows_clipped(const float* x, int64_t rows, int64_t K, int64
         scales[r] = s;
         for (int64_t k = 0; k < K; ++k) q[r * ldq + k] = oracle_e4m3_encode(xr[k] / s);
     }
+}
+
+/* ----------------------------------------------------------- KV cache -- */
+
+/* Per-channel KV scales ([DSV4] §2.2: one scale per latent dimension;
+ * [SP512K] §3.3 and [DEPLOY] §2.3: per-channel scales):
+ *   scale[c] = max(fl32(max_t |kv[t,c]| / fmt_max), 1e-12f),
+ * fmt_max = 448 (E4M3) or 57344 (E5M2, the KV format of [DSV4] §2.1).    */
+void oracle_kv_channel_scales(const float* kv, int64_t T, int64_t C, int64_t ld, int fmt, float* scales) {
+    const float fmax = fmt == 1 ? 57344.0f : 448.0f;
+#pragma omp parallel for schedule(static)
+    for (int64_t c = 0; c < C; ++c) {
+        float amax = 0.0f;
+        for (int64_t t = 0; t < T; ++t) {
+            float a = fabsf(kv[t * ld + c]);
+            if (a > amax) amax = a;
+        }
+        float s = amax / fmax;
+        if (s < 1e-12f) s = 1e-12f;
+        scales[c] = s;
+    }
+}
+
+/* Quantize T tokens of KV into a paged cache of num_slots rows: token t goes
+ * to cache row slot[t] (a block index times the block size plus the offset
+ * in the block, as the block table of [SP512K] §3.3 resolves it).  A slot
+ * outside [0, num_slots) (padding tokens carry -1) skips the token.  The
+ * scale is floored at 1e-12f as everywhere else.
+ *   cache[slot[t], c] = enc_fmt(fl32(kv[t,c] / scale[c]))                 */
+void oracle_kv_quantize(const float* kv, int64_t T, int64_t C, int64_t ld, const float* scales, int fmt,
+                        const int32_t* slot, uint8_t* cache, int64_t num_slots) {
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        if (slot[t] < 0 || slot[t] >= num_slots) continue;
+        for (int64_t c = 0; c < C; ++c) {
+            float s = scales[c] < 1e-12f ? 1e-12f : scales[c];
+            float q = kv[t * ld + c] / s;
+            cache[(int64_t)slot[t] * C + c] = fmt == 1 ? oracle_e5m2_encode(q) : oracle_e4m3_encode(q);
+        }
+    }
+}
+
+/* Read back: out[t,c] = fl32(dec_fmt(cache[slot[t], c]) * scale[c]) with the
+ * same floored scale; a slot outside [0, num_slots) gives a row of zeros.  */
+void oracle_kv_dequantize(const uint8_t* cache, int64_t num_slots, const int32_t* slot, int64_t T, int64_t C,
+                          const float* scales, int fmt, float* out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t c = 0; c < C; ++c) {
+            if (slot[t] < 0 || slot[t] >= num_slots) {
+                out[t * C + c] = 0.0f;
+                continue;
+            }
+            uint8_t code = cache[(int64_t)slot[t] * C + c];
+            float s = scales[c] < 1e-12f ? 1e-12f : scales[c];
+            float d = (float)(fmt == 1 ? oracle_e5m2_decode(code) : oracle_e4m3_decode(code));
+            out[t * C + c] = d * s;
+        }
 }
 
 /* --------------------------------------------------------------- GEMM ---- */

@@ -20,6 +20,8 @@ _lib = None
 STREAM_X = 10
 STREAM_W = 20
 STREAM_ROUTE = 30
+STREAM_KV = 40
+STREAM_KV_SLOTS = 50
 STREAM_EXPERT_W = 1000  # expert e uses streams 1000 + 2e, 1000 + 2e + 1
 
 
@@ -47,6 +49,10 @@ def lib():
         L.synth_activations.argtypes = [u64, u64, i64, i64, i64, i64, f32, vp, vp]
         L.synth_weights.restype = None
         L.synth_weights.argtypes = [u64, u64, i64, i64, i64, i64, vp]
+        L.synth_kv.restype = None
+        L.synth_kv.argtypes = [u64, u64, i64, i64, i64, i64, f32, vp]
+        L.synth_permutation.restype = None
+        L.synth_permutation.argtypes = [u64, i64, vp]
         L.synth_routing.restype = ctypes.c_int
         L.synth_routing.argtypes = [u64, u64, i64, i64, i64, f64, vp, vp, vp]
         _lib = L
@@ -96,6 +102,29 @@ def routing(T, E, topk, zipf_s, seed=0, stream=STREAM_ROUTE):
     return te.reshape(T, topk), rt, off
 
 
+def kv_activations(T, C, seed=0, n_outliers=None, outlier_mult=20.0, stream=STREAM_KV, out=None):
+    """KV rows [T, C] fp32: N(0,1) times a per-channel gain exp(0.5 N(0,1)),
+    1% of the channels (by default) with a further `outlier_mult` gain."""
+    kv = np.empty((T, C), dtype=np.float32) if out is None else out
+    assert kv.dtype == np.float32 and kv.shape == (T, C) and kv.flags.c_contiguous
+    n_out = n_outlier_channels(C) if n_outliers is None else n_outliers
+    lib().synth_kv(seed, stream, T, C, C, n_out, outlier_mult, _ptr(kv))
+    return kv
+
+
+def kv_slot_mapping(T, block_size, num_blocks, seed=0, stream=STREAM_KV_SLOTS):
+    """Cache slots of T tokens of one sequence in a paged cache: the sequence's
+    logical block i sits in physical block perm[i] of a random permutation of
+    num_blocks blocks, so token t goes to perm[t // B] * B + t % B.  int32."""
+    nb_used = -(-T // block_size)
+    if nb_used > num_blocks:
+        raise ValueError("kv_slot_mapping: the cache has too few blocks")
+    perm = np.empty(max(num_blocks, 1), dtype=np.int64)
+    lib().synth_permutation(lib().synth_stream_key(seed, stream), num_blocks, _ptr(perm))
+    t = np.arange(T, dtype=np.int64)
+    return (perm[t // block_size] * block_size + t % block_size).astype(np.int32)
+
+
 def n_outlier_channels(K):
     """1% of the channels (rounded), the outlier share of the decode/prefill workloads."""
     return int(math.floor(0.01 * K + 0.5))
@@ -117,6 +146,9 @@ WORKLOADS = {
                                desc="Llama-3-70B prefill square GEMM M=N=K=8192 with fused quantize"),
     "moe-64x2048x7168": dict(kind="moe", T=4096, E=64, topk=8, zipf=1.1, K=7168, N=2048, n_out=None,
                              mult=50.0, desc="MoE 64 experts K=7168 N=2048, 4096 tokens top-8 Zipf(1.1)"),
+    "kv-llama3-70b-32k": dict(kind="kv", T=32768, C=2048, block=16, fmt="e5m2",
+                              desc="Llama-3-70B KV cache, one layer (8 KV heads x 128, K and V), "
+                                   "32768-token prefill into 16-token pages, E5M2"),
 }
 
 

@@ -178,3 +178,33 @@ int synth_routing(uint64_t seed, uint64_t stream, int64_t T, int64_t E, int64_t 
     free(logw);
     return 0;
 }
+
+/*
+ * KV activations [T, C] (row stride ld): N(0,1) times a per-channel gain
+ * exp(0.5 g_c), g_c ~ N(0,1), with `n_out` outlier channels further scaled by
+ * `out_mult`.  Streams: base (values), base+1 (gains), base+2 (outliers).
+ */
+void synth_kv(uint64_t seed, uint64_t stream, int64_t T, int64_t C, int64_t ld, int64_t n_out, float out_mult,
+              float* kv) {
+    uint64_t kz = synth_stream_key(seed, stream), kg = synth_stream_key(seed, stream + 1);
+    uint64_t kc = synth_stream_key(seed, stream + 2);
+    double* gain = (double*)malloc(sizeof(double) * (size_t)(C > 0 ? C : 1));
+    int64_t* c = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n_out > 0 ? n_out : 1));
+    for (int64_t j = 0; j < C; ++j) gain[j] = exp(0.5 * normal_at(kg, (uint64_t)j));
+    synth_choose(kc, C, n_out, c);
+    for (int64_t i = 0; i < n_out; ++i) gain[c[i]] *= (double)out_mult;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t j = 0; j < C; ++j) kv[t * ld + j] = (float)(gain[j] * normal_at(kz, (uint64_t)(t * C + j)));
+    free(c);
+    free(gain);
+}
+
+/* A uniformly random permutation of 0..n-1 (Fisher-Yates). */
+void synth_permutation(uint64_t key, int64_t n, int64_t* perm) {
+    for (int64_t i = 0; i < n; ++i) perm[i] = i;
+    for (int64_t i = n - 1; i > 0; --i) {
+        int64_t j = (int64_t)(sm64_at(key, (uint64_t)i) % (uint64_t)(i + 1));
+        int64_t t = perm[i]; perm[i] = perm[j]; perm[j] = t;
+    }
+}

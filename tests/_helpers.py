@@ -17,6 +17,18 @@ def torch_e4m3_values():
     return codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
 
 
+def torch_e5m2_values():
+    """float64 value of each of the 256 codes, decoded by PyTorch's float8_e5m2."""
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    return codes.view(torch.float8_e5m2).to(torch.float64).numpy()
+
+
+def torch_encode_e5m2(v):
+    """PyTorch's float32 -> float8_e5m2 cast, as uint8 codes."""
+    t = torch.from_numpy(np.ascontiguousarray(v, dtype=np.float32))
+    return t.to(torch.float8_e5m2).view(torch.uint8).numpy()
+
+
 def torch_encode(v):
     """PyTorch's float32 -> float8_e4m3fn cast, as uint8 codes."""
     t = torch.from_numpy(np.ascontiguousarray(v, dtype=np.float32))
@@ -37,13 +49,18 @@ def pin_lib():
                                        ctypes.POINTER(ctypes.c_uint32)]
         L.pin_encode_one.restype = ctypes.c_uint8
         L.pin_encode_one.argtypes = [ctypes.c_void_p, ctypes.c_float]
+        L.pin_encode_range_n.restype = ctypes.c_uint64
+        L.pin_encode_range_n.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_uint64,
+                                         ctypes.c_uint64, ctypes.POINTER(ctypes.c_uint32)]
+        L.pin_encode_one_n.restype = ctypes.c_uint8
+        L.pin_encode_one_n.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_float]
         _pin_lib = L
     return _pin_lib
 
 
-def read_fixed_points():
+def read_fixed_points(name="e4m3_fixed_points.txt"):
     rows = []
-    with open(os.path.join(_HERE, "golden", "e4m3_fixed_points.txt")) as f:
+    with open(os.path.join(_HERE, "golden", name)) as f:
         for line in f:
             line = line.strip()
             if not line or line.startswith("#"):

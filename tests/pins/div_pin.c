@@ -8,10 +8,11 @@
  * rounded to binary32, which is correctly rounded because 53 >= 2 * 24 + 2.
  *
  * Cases: random scales over the whole range a row scale can take
- * (1e-12 .. FLT_MAX / 448) with random |x| <= 448 s, and, for a list of
- * scales, every x within a few ulps of (midpoint between two consecutive
- * E4M3 magnitudes) * s and of (E4M3 magnitude) * s -- the quotients where a
- * one-ulp error would change the E4M3 code.
+ * (1e-12 .. FLT_MAX / 448) with random |x| <= 448 s or <= 57344 s; any
+ * finite x (quotients that overflow included); and, for a list of scales,
+ * every x within a few ulps of (midpoint between two consecutive E4M3 or
+ * E5M2 magnitudes) * s and of (FP8 magnitude) * s -- the quotients where a
+ * one-ulp error would change the code.
  */
 #include <math.h>
 #include <stdint.h>
@@ -27,9 +28,12 @@ static uint64_t sm64(uint64_t* st) {
     return z ^ (z >> 31);
 }
 
+/* The first quotient is clamped to +-2^20 (a med3 on the GPU) so that an
+ * fp32 overflow of x * r cannot turn the residual into inf - inf = NaN; a
+ * clamped quotient is far beyond every FP8 code's range and still saturates. */
 static float method(float x, float s) {
     const float r = (float)(1.0 / (double)s);
-    const float q0 = x * r;
+    const float q0 = fminf(fmaxf(x * r, -0x1p20f), 0x1p20f);
     const float e = fmaf(-q0, s, x);
     const float q1 = fmaf(e, r, q0);
     return copysignf(q1, x);
@@ -63,6 +67,35 @@ static float rand_scale(uint64_t* st) {
     return s;
 }
 
+/* Any finite x and any scale: below 2^20 the quotient is IEEE's (agree());
+ * at or above it, both quotients are beyond 2^17 -- past both FP8 formats'
+ * saturation points -- with the same sign. */
+uint64_t pin_div_any_x(uint64_t n, uint64_t seed, float* bad_x, float* bad_s) {
+    uint64_t bad = 0;
+#pragma omp parallel for reduction(+ : bad) schedule(static)
+    for (int64_t t = 0; t < (int64_t)(n >> 12); ++t) {
+        uint64_t st = seed * 0x9E3779B97F4A7C15ull + (uint64_t)t;
+        const float s = rand_scale(&st);
+        for (int i = 0; i < 4096; ++i) {
+            union { float f; uint32_t u; } b;
+            do { b.u = (uint32_t)sm64(&st); } while (!isfinite(b.f));
+            const float x = b.f;
+            const float q = method(x, s), ref = exact(x, s);
+            int ok;
+            if (fabsf(ref) < 0x1p20f)
+                ok = agree(q, ref);
+            else
+                ok = fabsf(q) >= 0x1p17f && signbit(q) == signbit(ref);
+            if (!ok) {
+                ++bad;
+                *bad_x = x;
+                *bad_s = s;
+            }
+        }
+    }
+    return bad;
+}
+
 uint64_t pin_div_random(uint64_t n, uint64_t seed, float* bad_x, float* bad_s) {
     uint64_t bad = 0;
 #pragma omp parallel for reduction(+ : bad) schedule(static)
@@ -70,10 +103,12 @@ uint64_t pin_div_random(uint64_t n, uint64_t seed, float* bad_x, float* bad_s) {
         uint64_t st = seed * 0x100000001B3ull + (uint64_t)t;
         const float s = rand_scale(&st);
         for (int i = 0; i < 4096; ++i) {
-            /* |x| <= 448 s: a random magnitude fraction with random exponent depth */
+            /* |x| <= 448 s (E4M3 rows) or <= 57344 s (E5M2 KV channels): a
+             * random magnitude fraction with random exponent depth */
             const double frac = (double)(sm64(&st) >> 11) * 0x1.0p-53;
             const int depth = (int)(sm64(&st) % 40);
-            float x = (float)(448.0 * (double)s * frac * exp2(-depth));
+            const double top = (t & 1) ? 57344.0 : 448.0;
+            float x = (float)(top * (double)s * frac * exp2(-depth));
             if (sm64(&st) & 1) x = -x;
             if (!agree(method(x, s), exact(x, s))) {
                 ++bad;
@@ -95,9 +130,20 @@ static int e4m3_mags(double* out) {
     return n;
 }
 
-uint64_t pin_div_boundaries(const float* scales, int n_scales, int ulps, uint64_t* checked) {
+/* E5M2 finite magnitudes (exponent bias 15, 2 mantissa bits, subnormals below 2^-14). */
+static int e5m2_mags(double* out) {
+    int n = 0;
+    for (int code = 0; code <= 0x7B; ++code) {
+        const int e = code >> 2, m = code & 3;
+        out[n++] = e == 0 ? ldexp((double)m, -16) : ldexp(1.0 + m / 4.0, e - 15);
+    }
+    return n;
+}
+
+/* fmt 0: E4M3 boundaries, 1: E5M2 boundaries. */
+uint64_t pin_div_boundaries(const float* scales, int n_scales, int ulps, int fmt, uint64_t* checked) {
     double mags[127];
-    const int nm = e4m3_mags(mags);
+    const int nm = fmt == 1 ? e5m2_mags(mags) : e4m3_mags(mags);
     double pts[2 * 127];
     int np = 0;
     for (int i = 0; i < nm; ++i) pts[np++] = mags[i];

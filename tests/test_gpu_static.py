@@ -80,3 +80,13 @@ def test_static_scale_through_the_gemm():
     ref, absref = oracle.gemm_ref(oqa, np.full(M, s, np.float32), qw, sc)
     r = oracle.tolerance_check(y, ref, absref)
     assert r["ok"], r
+
+
+def test_static_scale_far_below_the_data_saturates():
+    """x / s overflowing fp32 must still give the saturated code (+-448)."""
+    x = np.array([[3e38, -3e38, 1e30, -1e27] + [1.0] * 12], np.float32)
+    s = np.float32(1e-12)
+    q, _ = fp8.fp8_quantize_static(to_dev(x), to_dev(np.array([s], np.float32)))
+    want = oracle.quantize_static(x, s)
+    assert want[0, :4].tolist() == [0x7E, 0xFE, 0x7E, 0xFE]
+    assert_codes_equal(to_host(q), want, "static overflow")
