@@ -42,6 +42,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 KERNEL_SOURCES = {
     "skinny": ["gemm_skinny.hip", "device_common.hpp"],
     "mfma": ["gemm_mfma.hip", "device_common.hpp"],
+    "kv": ["kv_cache.hip", "device_common.hpp"],
 }
 
 
@@ -509,7 +510,7 @@ def bench_kv(args, w, dev, steps, warmup, graph, log):
     roof = dict(bound="hbm", achieved=round(q_ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                 frac=round(q_ach / HBM_PEAK_GBS, 4), kernel="kv_quantize_paged",
                 per_launch=f"{quant_bytes} algorithmic bytes (fp32 kv in, slots, scales, FP8 codes out)",
-                avg_launch_us=round(q_ms * 1e3, 3), traffic=None,
+                avg_launch_us=round(q_ms * 1e3, 3), traffic=read_traffic(args.workload, "kv", "kv_quantize_paged"),
                 others=dict(channel_scales=dict(kernels="kv_amax_partial + kv_scale_finish",
                                                 avg_us=round(sc_ms * 1e3, 3), achieved=round(gbs(scale_bytes, sc_ms), 1),
                                                 frac=round(gbs(scale_bytes, sc_ms) / HBM_PEAK_GBS, 4),

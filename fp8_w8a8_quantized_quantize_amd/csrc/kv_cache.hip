@@ -13,7 +13,10 @@
 // channels (one float4 of a row, one 32-bit word of codes) and walks down a
 // range of rows, so a wave touches 1 KB of fp32 or 256 B of codes per row,
 // contiguous, and the per-channel scale and its reciprocal are formed once
-// per thread, not per element.
+// per thread, not per element.  The fp32 stream that is read once (the
+// batch) and the one that is written once (the read back) go through
+// nontemporal loads and stores: measured on MI355X they lift the batch read
+// from about 5.4 to 6.4 TB/s and the read back from 4.6 to 6.7 TB/s.
 #include <algorithm>
 
 #include "device_common.hpp"
@@ -23,7 +26,18 @@ namespace fp8k {
 
 constexpr float kE5M2Max = 57344.0f;  // largest finite E5M2 value
 constexpr int kKvThreads = 256;       // 4 channels per thread: 1024 channels per workgroup
-constexpr int kKvUnroll = 8;          // rows in flight per thread
+constexpr int kKvUnroll = 8;          // rows in flight per thread (maximum pass, read back)
+constexpr int kKvQuantUnroll = 16;    // rows in flight per thread (quantize)
+
+__device__ __forceinline__ float4 load_nt(const float4* p) {
+    const v4f t = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p));
+    return make_float4(t[0], t[1], t[2], t[3]);
+}
+
+__device__ __forceinline__ void store_nt(const float4& v, float4* p) {
+    const v4f t = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(t, reinterpret_cast<v4f*>(p));
+}
 
 // Two fp32 -> FP8 codes in bytes [2*HI, 2*HI+1] of `old`, clamped to the
 // format's largest finite value first so the conversion saturates; the
@@ -75,11 +89,11 @@ __global__ __launch_bounds__(kKvThreads) void kv_amax_partial(const float* __res
     for (; r + kKvUnroll <= r1; r += kKvUnroll) {
         float4 v[kKvUnroll];
 #pragma unroll
-        for (int i = 0; i < kKvUnroll; ++i) v[i] = p[(int64_t)(r + i) * ld4];
+        for (int i = 0; i < kKvUnroll; ++i) v[i] = load_nt(p + (int64_t)(r + i) * ld4);
 #pragma unroll
         for (int i = 0; i < kKvUnroll; ++i) m = abs_max4(m, v[i]);
     }
-    for (; r < r1; ++r) m = abs_max4(m, p[(int64_t)r * ld4]);
+    for (; r < r1; ++r) m = abs_max4(m, load_nt(p + (int64_t)r * ld4));
     part[(int64_t)g * chunks + blockIdx.y] = m;
 }
 
@@ -140,21 +154,21 @@ __global__ __launch_bounds__(kKvThreads) void kv_quantize_paged(const float* __r
     uint32_t* out = reinterpret_cast<uint32_t*>(cache) + g;
     const int64_t c4 = C4;
     int r = r0;
-    for (; r + kKvUnroll <= r1; r += kKvUnroll) {
-        float4 v[kKvUnroll];
-        int sl[kKvUnroll];
+    for (; r + kKvQuantUnroll <= r1; r += kKvQuantUnroll) {
+        float4 v[kKvQuantUnroll];
+        int sl[kKvQuantUnroll];
 #pragma unroll
-        for (int i = 0; i < kKvUnroll; ++i) {
+        for (int i = 0; i < kKvQuantUnroll; ++i) {
             sl[i] = slot[r + i];
-            v[i] = p[(int64_t)(r + i) * ld4];
+            v[i] = load_nt(p + (int64_t)(r + i) * ld4);
         }
 #pragma unroll
-        for (int i = 0; i < kKvUnroll; ++i)
+        for (int i = 0; i < kKvQuantUnroll; ++i)
             if (sl[i] >= 0 && sl[i] < num_slots) out[(int64_t)sl[i] * c4] = kv_encode4<FMT>(v[i], rs);
     }
     for (; r < r1; ++r) {
         const int s = slot[r];
-        if (s >= 0 && s < num_slots) out[(int64_t)s * c4] = kv_encode4<FMT>(p[(int64_t)r * ld4], rs);
+        if (s >= 0 && s < num_slots) out[(int64_t)s * c4] = kv_encode4<FMT>(load_nt(p + (int64_t)r * ld4), rs);
     }
 }
 
@@ -186,14 +200,14 @@ __global__ __launch_bounds__(kKvThreads) void kv_dequantize_paged(const uint8_t*
 #pragma unroll
         for (int i = 0; i < kKvUnroll; ++i) {
             const float4 d = kv_decode4<FMT>(w[i]);
-            out[(int64_t)(r + i) * ldo4] = make_float4(d.x * s.x, d.y * s.y, d.z * s.z, d.w * s.w);
+            store_nt(make_float4(d.x * s.x, d.y * s.y, d.z * s.z, d.w * s.w), out + (int64_t)(r + i) * ldo4);
         }
     }
     for (; r < r1; ++r) {
         const int sl = slot[r];
         const uint32_t w = (sl >= 0 && sl < num_slots) ? in[(int64_t)sl * c4] : 0u;
         const float4 d = kv_decode4<FMT>(w);
-        out[(int64_t)r * ldo4] = make_float4(d.x * s.x, d.y * s.y, d.z * s.z, d.w * s.w);
+        store_nt(make_float4(d.x * s.x, d.y * s.y, d.z * s.z, d.w * s.w), out + (int64_t)r * ldo4);
     }
 }
 
@@ -201,18 +215,21 @@ __global__ __launch_bounds__(kKvThreads) void kv_dequantize_paged(const uint8_t*
 
 namespace {
 
-constexpr int64_t kKvTargetBlocks = 2048;  // 8 workgroups of 256 threads per CU
-constexpr int64_t kKvMaxChunks = 1024;
+// Grid sizes, from a sweep on MI355X over a 32768 x 2048 batch: the maximum
+// pass is fastest with one workgroup per CU, each streaming long column
+// ranges (42 us vs 54 us at 4 per CU); quantize and read back with about 8
+// per CU.
+constexpr int64_t kKvAmaxBlocks = 256;
+constexpr int64_t kKvTargetBlocks = 2048;
 constexpr int64_t kKvMinRows = 16;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Row ranges per workgroup so the grid has about kKvTargetBlocks workgroups
-// and no workgroup takes fewer than kKvMinRows rows (or all of them).
-int64_t rows_per_block(int64_t T, int64_t col_blocks, int64_t max_row_blocks) {
-    int64_t row_blocks = ceil_div(kKvTargetBlocks, col_blocks);
+// Row ranges per workgroup so the grid has about `target` workgroups and no
+// workgroup takes fewer than kKvMinRows rows (or all of them).
+int64_t rows_per_block(int64_t T, int64_t col_blocks, int64_t target) {
+    int64_t row_blocks = ceil_div(target, col_blocks);
     row_blocks = std::min<int64_t>(row_blocks, std::max<int64_t>(1, ceil_div(T, kKvMinRows)));
-    row_blocks = std::min<int64_t>(row_blocks, max_row_blocks);
     return std::max<int64_t>(1, ceil_div(T, row_blocks));
 }
 
@@ -220,7 +237,7 @@ int64_t rows_per_block(int64_t T, int64_t col_blocks, int64_t max_row_blocks) {
 
 KvChunks kv_amax_chunks(int64_t T, int64_t C) {
     const int64_t col_blocks = ceil_div(C / 4, kKvThreads);
-    const int64_t rpc = rows_per_block(T, std::max<int64_t>(col_blocks, 1), kKvMaxChunks);
+    const int64_t rpc = rows_per_block(T, std::max<int64_t>(col_blocks, 1), kKvAmaxBlocks);
     return KvChunks{(int)rpc, (int)std::max<int64_t>(1, ceil_div(T, rpc))};
 }
 
@@ -248,7 +265,7 @@ hipError_t launch_kv_quantize_paged(const float* kv, int64_t T, int64_t C, int64
                                     const int32_t* slot, uint8_t* cache, int64_t num_slots, hipStream_t stream) {
     const int C4 = (int)(C / 4);
     const int64_t cb = ceil_div(C4, kKvThreads);
-    const int64_t rpb = rows_per_block(T, cb, INT32_MAX);
+    const int64_t rpb = rows_per_block(T, cb, kKvTargetBlocks);
     const dim3 grid((unsigned)cb, (unsigned)ceil_div(T, rpb));
     if (fmt == kKvE5M2)
         hipLaunchKernelGGL(kv_quantize_paged<kKvE5M2>, grid, dim3(kKvThreads), 0, stream, kv, ldkv / 4, scales, slot,
@@ -264,7 +281,7 @@ hipError_t launch_kv_dequantize_paged(const uint8_t* cache, int64_t num_slots, c
                                       hipStream_t stream) {
     const int C4 = (int)(C / 4);
     const int64_t cb = ceil_div(C4, kKvThreads);
-    const int64_t rpb = rows_per_block(T, cb, INT32_MAX);
+    const int64_t rpb = rows_per_block(T, cb, kKvTargetBlocks);
     const dim3 grid((unsigned)cb, (unsigned)ceil_div(T, rpb));
     if (fmt == kKvE5M2)
         hipLaunchKernelGGL(kv_dequantize_paged<kKvE5M2>, grid, dim3(kKvThreads), 0, stream, cache, num_slots, slot,

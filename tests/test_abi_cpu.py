@@ -239,8 +239,9 @@ def test_static_clipped_and_calibration_validation():
 def test_kv_validation():
     L = fp8.lib()
     E4, E5 = fp8.FP8_KV_E4M3, fp8.FP8_KV_E5M2
-    # workspace: one fp32 partial maximum per channel and row chunk (at most 1024 chunks)
-    assert L.fp8_kv_scales_workspace_bytes(32768, 2048) == 1024 * 2048 * 4
+    # workspace: one fp32 partial maximum per channel and row chunk (about 256 workgroups in all)
+    assert L.fp8_kv_scales_workspace_bytes(32768, 2048) == 128 * 2048 * 4
+    assert L.fp8_kv_scales_workspace_bytes(32768, 576) == 256 * 576 * 4
     assert L.fp8_kv_scales_workspace_bytes(0, 576) == 576 * 4          # one chunk; 2304 = 9 * 256
     assert L.fp8_kv_scales_workspace_bytes(0, 68) == 512              # rounded up to 256 bytes
     assert L.fp8_kv_scales_workspace_bytes(10, 6) == ctypes.c_size_t(-1).value     # C % 4
