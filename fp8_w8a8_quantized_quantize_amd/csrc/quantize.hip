@@ -23,6 +23,13 @@ constexpr int kQThreads = 256;
 constexpr int kQThreadsWide = 1024;
 constexpr int64_t kQWideRowsBelow = 512;
 
+// A row held in registers is read from HBM exactly once: nontemporal loads
+// keep it from displacing cache lines that are still useful.
+__device__ __forceinline__ float4 load_nt(const float4* p) {
+    const v4f t = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p));
+    return make_float4(t[0], t[1], t[2], t[3]);
+}
+
 template <int T>
 __device__ __forceinline__ float block_max(float v, float* red) {
     constexpr int W = T / kWave;
@@ -67,7 +74,12 @@ __global__ __launch_bounds__(T) void quantize_rows_regs(const float* __restrict_
         for (int i = 0; i < VPT; ++i) {
             const int j = i * T + threadIdx.x;
             if (j < K4) {
-                v[i] = xr[j];
+                // many rows (256-thread blocks): a stream read once, kept out of
+                // the caches; decode batches keep plain loads (measured faster)
+                if constexpr (T == kQThreads)
+                    v[i] = load_nt(xr + j);
+                else
+                    v[i] = xr[j];
                 if constexpr (MODE != 1) amax = absmax4(amax, v[i]);
             }
         }
