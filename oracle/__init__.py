@@ -61,6 +61,12 @@ def lib():
         L.oracle_kv_quantize.argtypes = [vp, i64, i64, i64, vp, ctypes.c_int, vp, vp, i64]
         L.oracle_kv_dequantize.restype = None
         L.oracle_kv_dequantize.argtypes = [vp, i64, vp, i64, i64, vp, ctypes.c_int, vp]
+        L.oracle_mx_scale_code.restype = ctypes.c_uint8
+        L.oracle_mx_scale_code.argtypes = [ctypes.c_float]
+        L.oracle_quantize_mx.restype = None
+        L.oracle_quantize_mx.argtypes = [vp, i64, i64, i64, vp, i64, vp]
+        L.oracle_gemm_mx_ref_sampled.restype = None
+        L.oracle_gemm_mx_ref_sampled.argtypes = [vp, i64, vp, vp, i64, vp, i64, vp, vp, i64, vp, vp]
         L.oracle_gemm_ref.restype = None
         L.oracle_gemm_ref.argtypes = [vp, i64, vp, vp, i64, vp, i64, i64, i64, vp, vp]
         L.oracle_gemm_ref_sampled.restype = None
@@ -176,6 +182,51 @@ def kv_dequantize(cache, slot, scales, fmt):
     lib().oracle_kv_dequantize(_p(cache), num_slots, _p(slot), slot.size, C, _p(_c(scales, np.float32)), int(fmt),
                                _p(out))
     return out
+
+
+MX_BLOCK = 32
+
+
+def mx_scale_code(amax):
+    """E8M0 code (exponent + 127) of the block scale for a block maximum amax."""
+    return int(lib().oracle_mx_scale_code(float(np.float32(amax))))
+
+
+def quantize_mx(x):
+    """Block-scaled quantization of fp32 x [rows, K] (K % 32 == 0) ->
+    (codes uint8 [rows, K], scale codes uint8 [rows, K/32])."""
+    x = _c(x, np.float32)
+    rows, K = x.shape
+    assert K % MX_BLOCK == 0
+    q = np.empty((rows, K), dtype=np.uint8)
+    sc = np.empty((rows, K // MX_BLOCK), dtype=np.uint8)
+    lib().oracle_quantize_mx(_p(x), rows, K, K, _p(q), K, _p(sc))
+    return q, sc
+
+
+def gemm_mx_ref_sampled(qa, sa, qw, sw, ms, ns):
+    """Block-scaled GEMM reference at (ms[i], ns[i]) -> (ref, absref) float64."""
+    qa, qw = _c(qa, np.uint8), _c(qw, np.uint8)
+    sa, sw = _c(sa, np.uint8), _c(sw, np.uint8)
+    ms, ns = _c(ms, np.int64), _c(ns, np.int64)
+    M, K = qa.shape
+    N = qw.shape[0]
+    assert qw.shape[1] == K and sa.shape == (M, K // MX_BLOCK) and sw.shape == (N, K // MX_BLOCK)
+    assert ms.shape == ns.shape
+    assert ms.size == 0 or (ms.min() >= 0 and ms.max() < M and ns.min() >= 0 and ns.max() < N)
+    ref = np.empty(ms.size, dtype=np.float64)
+    ab = np.empty(ms.size, dtype=np.float64)
+    lib().oracle_gemm_mx_ref_sampled(_p(qa), K, _p(sa), _p(qw), K, _p(sw), K, _p(ms), _p(ns), ms.size, _p(ref),
+                                     _p(ab))
+    return ref, ab
+
+
+def gemm_mx_ref(qa, sa, qw, sw):
+    """Full block-scaled GEMM reference -> (ref [M,N], absref [M,N]) float64."""
+    M, N = qa.shape[0], qw.shape[0]
+    mm, nn = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    r, a = gemm_mx_ref_sampled(qa, sa, qw, sw, mm.ravel(), nn.ravel())
+    return r.reshape(M, N), a.reshape(M, N)
 
 
 def quantize_static(x, scale):

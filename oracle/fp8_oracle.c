@@ -21,6 +21,9 @@
  *           +-448; the KV-cache scale sketch).
  *   [SP512K] "512K context on 8 x H20" (hotelren.com), §3.3 (paged KV cache
  *           in FP8 with per-channel scales).
+ * Block scales: [DSV4] §2.4 (per-group/block scales: one scale per small
+ * block of a tensor) and §4.2 (per-group where activation ranges jump);
+ * [DEPLOY] §7.1 (MXFP8: FP8 elements with a shared scale per block).
  *
  * Readings where the pages leave a step open (all float arithmetic below is
  * IEEE binary32/binary64 with round-to-nearest-even; build without
@@ -348,6 +351,81 @@ int oracle_grouped_ref_sampled(const uint8_t* qa, const float* s_tok, const int3
 }
 
 /* ----------------------------------------------------------- BF16 -------- */
+
+/* ------------------------------------------------------ block scales -- */
+
+/* Block-scaled ("MX") quantization.  Every 32 consecutive elements of a row
+ * share one scale that is a power of two, stored as its exponent byte
+ * (E8M0: code c means 2^(c - 127)).  Readings: the block is 32 elements
+ * (the open MX format; [DEPLOY] §7.1 says 16); the scale is the pages'
+ * absmax/448 scale ([L3] §3.1, 1e-12 floor) rounded up to a power of two,
+ *   v = max(fl32(amax / 448), 1e-12f),  e = smallest integer with 2^e >= v,
+ * so |x| / 2^e <= 448 and no element of the block is clipped; the codes are
+ * enc(x / 2^e) (a division by a power of two, exact unless the quotient is
+ * an fp32 subnormal, where it rounds once like any IEEE division).        */
+static int mx_exponent(float v) {
+    int e2;
+    double m = frexp((double)v, &e2); /* v = m * 2^e2, m in [0.5, 1) */
+    return m == 0.5 ? e2 - 1 : e2;
+}
+
+uint8_t oracle_mx_scale_code(float amax) {
+    float v = amax / 448.0f;
+    if (v < 1e-12f) v = 1e-12f;
+    return (uint8_t)(mx_exponent(v) + 127);
+}
+
+/* x [rows, K] (K % 32 == 0) -> codes q [rows, K] (ldq), scale codes
+ * sc [rows, K / 32] (row-major, no padding). */
+void oracle_quantize_mx(const float* x, int64_t rows, int64_t K, int64_t ldx, uint8_t* q, int64_t ldq,
+                        uint8_t* sc) {
+    const int64_t nb = K / 32;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t b = 0; b < nb; ++b) {
+            const float* xb = x + r * ldx + 32 * b;
+            float amax = 0.0f;
+            for (int i = 0; i < 32; ++i)
+                if (fabsf(xb[i]) > amax) amax = fabsf(xb[i]);
+            const uint8_t c = oracle_mx_scale_code(amax);
+            const double scale = ldexp(1.0, (int)c - 127);
+            sc[r * nb + b] = c;
+            for (int i = 0; i < 32; ++i) q[r * ldq + 32 * b + i] = oracle_e4m3_encode((float)((double)xb[i] / scale));
+        }
+}
+
+/* Block-scaled GEMM reference at the listed (m, n) pairs:
+ *   ref = sum_k dec(a[m,k]) dec(w[n,k]) 2^(sa[m,k/32] - 127) 2^(sw[n,k/32] - 127)
+ *   absref = the same sum of magnitudes.  Each block's sum is exact in
+ * binary64; adding the scaled block sums rounds only in binary64 (relative
+ * error about 2^-53 of absref).  sa [M, K/32], sw [N, K/32]. */
+static void mx_dot(const uint8_t* a, const uint8_t* sa, const uint8_t* w, const uint8_t* sw, int64_t K, double* ref,
+                   double* absref) {
+    double D = 0.0, A = 0.0;
+    for (int64_t b = 0; b < K / 32; ++b) {
+        double d = 0.0, ab = 0.0;
+        for (int i = 0; i < 32; ++i) {
+            double p = g_dec[a[32 * b + i]] * g_dec[w[32 * b + i]];
+            d += p;
+            ab += fabs(p);
+        }
+        double s = ldexp(1.0, (int)sa[b] + (int)sw[b] - 254);
+        D += d * s;
+        A += ab * s;
+    }
+    *ref = D;
+    *absref = A;
+}
+
+void oracle_gemm_mx_ref_sampled(const uint8_t* qa, int64_t lda, const uint8_t* sa, const uint8_t* qw, int64_t ldw,
+                                const uint8_t* sw, int64_t K, const int64_t* ms, const int64_t* ns, int64_t count,
+                                double* ref, double* absref) {
+    dec_table();
+    const int64_t nb = K / 32;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < count; ++i)
+        mx_dot(qa + ms[i] * lda, sa + ms[i] * nb, qw + ns[i] * ldw, sw + ns[i] * nb, K, ref + i, absref + i);
+}
 
 /* Nearest bfloat16 (1-8-7 format) of a double, ties to even, as bits.  Used
  * only to report how many GPU outputs equal the correctly rounded reference. */
