@@ -63,6 +63,9 @@ def parse():
     ap.add_argument("--act", choices=("dynamic", "static", "clipped"), default="dynamic",
                     help="activation scales: per-token absmax (default, the fused call), a static per-tensor "
                          "scale calibrated as the P99.9 of |x|, or per-token scales clipped at the P99.99 of |x|")
+    ap.add_argument("--scales", choices=("token", "mx"), default="token",
+                    help="token: per-token x per-channel scales (default); mx: 32-element block scales "
+                         "(fp8_quantize_mx + fp8_gemm_mx, dense workloads)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run 5 plain device copies of 512 MiB (reference for rocprofv3 FETCH/WRITE_SIZE)")
     ap.add_argument("--profile", action="store_true",
@@ -216,6 +219,11 @@ def main():
         return bench_fp8out(args, w, dev, steps, warmup, graph, log)
     if w["kind"] == "kv":
         return bench_kv(args, w, dev, steps, warmup, graph, log)
+    if args.scales == "mx":
+        if w["kind"] != "dense":
+            print("--scales mx is for the dense workloads", file=sys.stderr)
+            sys.exit(2)
+        return bench_mx(args, w, dev, steps, warmup, graph, log)
     if w["kind"] == "dense":
         M, N, K = w["M"], w["N"], w["K"]
         log(f"[bench] {args.workload}: generating inputs M={M} N={N} K={K}")
@@ -450,6 +458,68 @@ def bench_fp8out(args, w, dev, steps, warmup, graph, log):
         "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp8e4m3 (fp32 accumulate, e4m3 out)", "data": "synthetic (seeded; no dataset, no trained weights)",
+        "config": cfg, "roofline": roof, "cpu_baseline": None, "detail": extra,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def bench_mx(args, w, dev, steps, warmup, graph, log):
+    """One step = fp8_quantize_mx of the activations + fp8_gemm_mx against
+    block-scaled weights (quantized once, untimed): 32-element blocks along K
+    with power-of-two scales applied inside the K loop by the block-scaled
+    MFMA."""
+    import torch
+    import fp8_w8a8_quantized_quantize_amd as fp8
+    M, N, K = w["M"], w["N"], w["K"]
+    log(f"[bench] {args.workload} (block scales): generating inputs M={M} N={N} K={K}")
+    x, wt = gen_dense(w, args.seed)
+    wq, ws_ = fp8.fp8_quantize_mx(torch.from_numpy(wt).to(dev))
+    copies = max(1, math.ceil(ROTATE_BYTES / (N * K)))
+    wcopies = [(wq, ws_)] + [(wq.clone(), ws_.clone()) for _ in range(copies - 1)]
+    xd = torch.from_numpy(x).to(dev)
+    qa = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    sa = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(1, fp8.fp8_mx_workspace_bytes(M, N, K)), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        fp8.fp8_quantize_mx(xd, q=qa, scales=sa)
+        fp8.fp8_gemm_mx(qa, sa, wcopies[i % copies][0], wcopies[i % copies][1], y=y, ws=ws)
+
+    def gemm(i):
+        fp8.fp8_gemm_mx(qa, sa, wcopies[i % copies][0], wcopies[i % copies][1], y=y, ws=ws)
+
+    total_ms, per = time_loop(step, steps, warmup, graph)
+    gemm_ms, _ = time_loop(gemm, steps, warmup, graph)
+    ms, g_ms = total_ms / steps, gemm_ms / steps
+    flops = 2.0 * M * N * K
+    gemm_bytes = N * K + N * K // 32 + M * K + M * K // 32 + 2 * M * N
+    step_bytes = 4 * M * K + N * K + N * K // 32 + 2 * M * N
+    decode = M <= 64
+    if decode:
+        value, unit = step_bytes / (ms * 1e-3) / 1e9, "GB/s"
+        ach = gemm_bytes / (g_ms * 1e-3) / 1e9
+        roof = dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s", frac=round(ach / HBM_PEAK_GBS, 4),
+                    per_launch=f"{gemm_bytes} algorithmic bytes (codes + exponent bytes of both operands, bf16 y)")
+        kernel = "gemm_skinny_kernel (block-scaled)"
+    else:
+        value, unit = flops / (ms * 1e-3) / 1e12, "TFLOP/s"
+        ach = flops / (g_ms * 1e-3) / 1e12
+        roof = dict(bound="mfma", achieved=round(ach, 1), peak=FP8_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=round(ach / FP8_PEAK_TFLOPS, 4), per_launch=f"{flops:.6g} FLOP")
+        kernel = "gemm_mfma_kernel (block-scaled)"
+    roof.update(kernel=kernel, avg_launch_us=round(g_ms * 1e3, 3), traffic=None)
+    cfg = dict(workload=args.workload, M=M, N=N, K=K, seed=args.seed, weight_copies=copies,
+               step="fp8_quantize_mx + fp8_gemm_mx", scales="32-element blocks, power-of-two (E8M0)", out="bf16")
+    extra = dict(timing="hip-graph replay of the steps" if graph else "eager launches", step_us=round(ms * 1e3, 3),
+                 step_tflops=round(flops / (ms * 1e-3) / 1e12, 2))
+    if per:
+        extra.update(step_us_median=round(pct(per, 0.5) * 1e3, 3))
+    out = {
+        "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8e4m3 with e8m0 block scales (fp32 accumulate, bf16 out)",
+        "data": "synthetic (seeded; no dataset, no trained weights)",
         "config": cfg, "roofline": roof, "cpu_baseline": None, "detail": extra,
     }
     print(json.dumps(out), flush=True)

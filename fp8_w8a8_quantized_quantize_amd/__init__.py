@@ -34,7 +34,8 @@ FP8_ERR_DEVICE = 4
 EXPORTS = ("fp8_quantize_per_token", "fp8_quantize_static", "fp8_quantize_per_token_clipped",
            "fp8_calibrate_percentile", "fp8_calibrate_workspace_bytes", "fp8_gemm_scaled", "fp8_quant_gemm_fused", "fp8_gemm_scaled_fp8out",
            "fp8_gemm_grouped_scaled", "fp8_workspace_bytes", "fp8_fp8out_workspace_bytes",
-           "fp8_grouped_workspace_bytes", "fp8_kv_channel_scales", "fp8_kv_scales_workspace_bytes",
+           "fp8_grouped_workspace_bytes", "fp8_quantize_mx", "fp8_gemm_mx", "fp8_mx_workspace_bytes",
+           "fp8_kv_channel_scales", "fp8_kv_scales_workspace_bytes",
            "fp8_kv_quantize_paged", "fp8_kv_dequantize_paged", "fp8_status_string")
 
 _lib = None
@@ -79,6 +80,12 @@ def lib():
         L.fp8_workspace_bytes.argtypes = [i64, i64, i64]
         L.fp8_grouped_workspace_bytes.restype = sz
         L.fp8_grouped_workspace_bytes.argtypes = [i64, i64, i64, i64, i64]
+        L.fp8_quantize_mx.restype = st
+        L.fp8_quantize_mx.argtypes = [vp, i64, i64, i64, vp, i64, vp, vp]
+        L.fp8_gemm_mx.restype = st
+        L.fp8_gemm_mx.argtypes = [vp, i64, vp, vp, i64, vp, vp, i64, i64, i64, i64, vp, sz, vp]
+        L.fp8_mx_workspace_bytes.restype = sz
+        L.fp8_mx_workspace_bytes.argtypes = [i64, i64, i64]
         L.fp8_kv_channel_scales.restype = st
         L.fp8_kv_channel_scales.argtypes = [vp, i64, i64, i64, st, vp, vp, sz, vp]
         L.fp8_kv_scales_workspace_bytes.restype = sz
@@ -218,6 +225,51 @@ def fp8_calibrate_percentile(x, num, den, stream=None):
            lib().fp8_calibrate_percentile(_ptr(x), x.numel(), int(num), int(den), _ptr(value), _ptr(scale), _ptr(ws),
                                           ws.numel(), _stream(stream)))
     return value, scale
+
+
+def fp8_mx_workspace_bytes(M, N, K):
+    return int(lib().fp8_mx_workspace_bytes(M, N, K))
+
+
+def fp8_quantize_mx(x, q=None, scales=None, stream=None):
+    """Block-scaled E4M3 quantization of fp32 x [M, K] (K % 32 == 0) ->
+    (q uint8 [M, K], scales uint8 [M, K/32] exponent bytes)."""
+    torch = _torch()
+    M, K, ldx = _rows(x, torch.float32, "x")
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((M, K // 32), dtype=torch.uint8, device=x.device)
+    _, _, ldq = _rows(q, torch.uint8, "q")
+    if not isinstance(scales, torch.Tensor) or scales.dtype != torch.uint8 or not scales.is_cuda \
+            or not scales.is_contiguous() or tuple(scales.shape) != (M, K // 32):
+        raise TypeError("scales: expected a contiguous uint8 CUDA tensor [M, K/32]")
+    _check("fp8_quantize_mx", lib().fp8_quantize_mx(_ptr(x), M, K, ldx, _ptr(q), ldq, _ptr(scales), _stream(stream)))
+    return q, scales
+
+
+def fp8_gemm_mx(qa, sa, qw, sw, y=None, ws=None, stream=None):
+    """y = bf16(sum over 32-blocks of 2^(sa + sw - 254) * block dot) for block-scaled
+    E4M3 operands qa [M, K], qw [N, K] with exponent bytes sa [M, K/32], sw [N, K/32]."""
+    torch = _torch()
+    M, K, lda = _rows(qa, torch.uint8, "qa")
+    N, K2, ldw = _rows(qw, torch.uint8, "qw")
+    if K2 != K:
+        raise ValueError("qa and qw disagree on K")
+    for t, name, rows in ((sa, "sa", M), (sw, "sw", N)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.uint8 or not t.is_cuda or not t.is_contiguous() \
+                or tuple(t.shape) != (rows, K // 32):
+            raise TypeError(f"{name}: expected a contiguous uint8 CUDA tensor [{rows}, K/32]")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=qa.device)
+    _, _, ldy = _rows(y, torch.bfloat16, "y")
+    if ws is None:
+        need = fp8_mx_workspace_bytes(M, N, K)
+        ws = torch.empty(need, dtype=torch.uint8, device=qa.device) if 0 < need < (1 << 62) else None
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check("fp8_gemm_mx", lib().fp8_gemm_mx(_ptr(qa), lda, _ptr(sa), _ptr(qw), ldw, _ptr(sw), _ptr(y), ldy, M, N, K,
+                                            _ptr(ws), ws_bytes, _stream(stream)))
+    return y
 
 
 FP8_KV_E4M3 = 0

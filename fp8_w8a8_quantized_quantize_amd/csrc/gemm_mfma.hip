@@ -53,6 +53,13 @@ __device__ __forceinline__ v16f mfma_32x32x64_e4m3(const v8i& a, const v8i& b, c
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
+// The same MFMA with block scales: the exponent byte that lane (r, g)
+// passes scales k [32g, 32g + 32) of the 64-k half for row r of its operand
+// (the fragment layout of read_frag below; measured on gfx950).
+__device__ __forceinline__ v16f mfma_32x32x64_e4m3_mx(const v8i& a, const v8i& b, const v16f& c, int sa, int sb) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
+
 __device__ __forceinline__ int dswz(int row) { return (row ^ (row >> 3)) & 7; }
 
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
@@ -135,6 +142,7 @@ struct MfmaArgs {
     const int32_t* row_token;  // grouped only
     const int32_t* offsets;
     int E;
+    MxScales mx;  // block-scaled operands (MX kernels only)
 };
 
 // Number of output tiles of expert e (row tiles x column tiles).
@@ -194,17 +202,30 @@ __device__ void find_expert_tile(const MfmaArgs& p, int b, int* sh) {
     __syncthreads();
 }
 
-template <int BN, int BM, int WN, int WM, int GROUP_M, bool GROUPED>
+// MX = true: block-scaled operands (dense only).  A stage also carries the
+// tile rows' 4 block-scale bytes (one 32-bit word per row, fetched by two more
+// DMA instructions per wave into a ring of their own); a lane reads its
+// fragment rows' words for stage s + 1 after the barrier of step s and passes
+// byte 2h + g for K half h; the tile scales of the epilogue are 1.  The
+// scales arrive chunk-major (word [kt][row], see transpose_mx_scales), so a
+// stage's words for consecutive rows are contiguous: the natural [row][kt]
+// order made every lane of a scale DMA touch its own cache line (measured:
+// 23 % slower on 8192^3).
+template <int BN, int BM, int WN, int WM, int GROUP_M, bool GROUPED, bool MX = false>
 __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_mfma_kernel(MfmaArgs p) {
+    static_assert(!(MX && GROUPED), "block scales: dense GEMM only");
     constexpr int NW = WN * WM;                 // waves: WN along the weight rows, WM along the activations
     constexpr int NTH = 64 * NW;
     constexpr int FN = BN / (32 * WN);          // 32-row weight fragments per wave
     constexpr int FM = BM / (32 * WM);          // 32-row activation fragments per wave
     constexpr int DA = BN / (8 * NW);           // DMA instructions per wave per stage, weights
     constexpr int DB = BM / (8 * NW);           // ... activations
-    constexpr int PER_STAGE = DA + DB;
+    constexpr int DS = MX ? (BN + BM) / (64 * NW) : 0;  // ... block-scale words (64 rows each)
+    constexpr int PER_STAGE = DA + DB + DS;
     constexpr int STAGE = (BN + BM) * kBK;
+    constexpr int SRING = 2 * STAGE + 4 * (BN + BM);    // block-scale ring: 2 x (BN + BM) words
     static_assert(DA * 8 * NW == BN && DB * 8 * NW == BM, "whole DMA instructions per wave");
+    static_assert(!MX || DS * 64 * NW == BN + BM, "whole scale DMA instructions per wave");
     static_assert(BM * BN * 2 <= 2 * STAGE, "the BF16 output tile must fit in the ring");
     int* sh = reinterpret_cast<int*>(smem + 2 * STAGE + 4 * (BN + BM));  // grouped tile lookup
 
@@ -272,10 +293,12 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_mfma_kernel(MfmaArgs p) 
     constexpr int RING = 2 * STAGE;
     float* s_ch_t = reinterpret_cast<float*>(smem + RING);
     float* s_tok_t = s_ch_t + BN;
-    for (int i = tid; i < BN; i += NTH) s_ch_t[i] = s_ch[min(n0 + i, p.N - 1)];
+    for (int i = tid; i < BN; i += NTH) s_ch_t[i] = MX ? 1.0f : s_ch[min(n0 + i, p.N - 1)];
     for (int i = tid; i < BM; i += NTH) {
         const int ml = min(i, rows_valid - 1);
-        if constexpr (GROUPED)
+        if constexpr (MX)
+            s_tok_t[i] = 1.0f;
+        else if constexpr (GROUPED)
             s_tok_t[i] = p.s_tok[p.row_token[row_begin + m0 + ml]];
         else
             s_tok_t[i] = p.s_tok[m0 + ml];
@@ -299,12 +322,31 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_mfma_kernel(MfmaArgs p) 
         bsrc[j] = p.qa + src_row * lda + ((lpos ^ dswz(row)) << 4);
     }
     const int nlast = p.N - 1;
+    // Block-scale DMA (MX): instruction j of this wave fetches the stage's
+    // scale words of tile rows (wave * DS + j) * 64 + lane, weight rows first.
+    const uint8_t* ssrc[DS + 1];
+    int64_t sstep[DS + 1];  // bytes between consecutive stages' words of a row
+    if constexpr (MX) {
+#pragma unroll
+        for (int j = 0; j < DS; ++j) {
+            const int r = (wave * DS + j) * 64 + lane;
+            ssrc[j] = r < BN ? p.mx.sw + 4 * (int64_t)min(n0 + r, nlast)
+                             : p.mx.sa + 4 * (int64_t)(m0 + min(r - BN, rows_valid - 1));
+            sstep[j] = 4 * (int64_t)(r < BN ? p.N : p.M);
+        }
+    }
+    auto issue_scale = [&](int kt, int slot, int j) {
+        __builtin_amdgcn_global_load_lds(ssrc[j] + kt * sstep[j],
+                                         smem + SRING + slot * 4 * (BN + BM) + (wave * DS + j) * 256, 4, 0, 0);
+    };
 
     // DMA instruction j (0 .. PER_STAGE - 1) of stage kt into ring slot `slot`.
     auto issue_one = [&](int kt, int slot, int j) {
         uint8_t* base = smem + slot * STAGE;
         const int koff = kt * kBK;
-        if (j < DA) {
+        if (j >= DA + DB) {
+            if constexpr (MX) issue_scale(kt, slot, j - DA - DB);
+        } else if (j < DA) {
             const int row = (wave * DA + j) * 8 + lrow;
             const int n = min(n0 + row, nlast);  // rows past N feed discarded columns
             dma16(qw + (int64_t)n * ldw + koff + ((lpos ^ dswz(row)) << 4), base + (wave * DA + j) * 1024);
@@ -325,6 +367,10 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_mfma_kernel(MfmaArgs p) 
         }
 #pragma unroll
         for (int j = 0; j < DB; ++j) dma16(bsrc[j] + koff, base + BN * kBK + (wave * DB + j) * 1024);
+        if constexpr (MX) {
+#pragma unroll
+            for (int j = 0; j < DS; ++j) issue_scale(kt, slot, j);
+        }
     };
 
     v16f acc[FN][FM];
@@ -343,6 +389,39 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_mfma_kernel(MfmaArgs p) 
         return read_frag(smem + slot * STAGE + BN * kBK, brow0 + b * 32, h, g);
     };
 
+    // Block scales (MX): the word of 4 exponent bytes of each of the lane's
+    // fragment rows; sc_* for the stage being computed, nx_* for the next.
+    constexpr int SF = MX ? 1 : 0;
+    uint32_t sc_a[FN * SF + 1], sc_b[FM * SF + 1], nx_a[FN * SF + 1], nx_b[FM * SF + 1];
+    auto read_scales = [&](int slot, uint32_t (&wa)[FN * SF + 1], uint32_t (&wb)[FM * SF + 1]) {
+        if constexpr (MX) {
+            const uint32_t* base = reinterpret_cast<const uint32_t*>(smem + SRING + slot * 4 * (BN + BM));
+#pragma unroll
+            for (int a = 0; a < FN; ++a) wa[a] = base[arow0 + a * 32];
+#pragma unroll
+            for (int b = 0; b < FM; ++b) wb[b] = base[BN + brow0 + b * 32];
+        }
+    };
+    auto next_scales = [&]() {
+        if constexpr (MX) {
+#pragma unroll
+            for (int a = 0; a < FN; ++a) sc_a[a] = nx_a[a];
+#pragma unroll
+            for (int b = 0; b < FM; ++b) sc_b[b] = nx_b[b];
+        }
+    };
+    // exponent byte for K half h of the current stage
+    auto sbyte = [&](uint32_t w, int h) { return (int)__builtin_amdgcn_ubfe(w, 16 * h + 8 * g, 8); };
+    auto mma = [&](const v8i& x, const v8i& w2, const v16f& c, int a, int b, int h) {
+        if constexpr (MX)
+            return mfma_32x32x64_e4m3_mx(x, w2, c, sbyte(sc_a[a], h), sbyte(sc_b[b], h));
+        else
+            return mfma_32x32x64_e4m3(x, w2, c);
+    };
+    // scale-word LDS instructions per step: the rows are 32 words apart, so
+    // the compiler pairs the reads into ds_read2_b32
+    constexpr int SR = MX ? (FN + FM) / 2 : 0;
+
     v8i fa[FN], fb[FM];
     if (KT > 0) {
         // prologue: stages 0 and 1 in flight, stage 0 landed everywhere,
@@ -351,6 +430,7 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_mfma_kernel(MfmaArgs p) 
         if (KT > 1) issue_stage(1, 1);
         wait_dma<PER_STAGE>(KT > 1 ? 1 : 0);
         block_barrier();
+        read_scales(0, sc_a, sc_b);
 #pragma unroll
         for (int b = 0; b < FM; ++b) fb[b] = read_b(0, 0, b);
 #pragma unroll
@@ -360,7 +440,7 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_mfma_kernel(MfmaArgs p) 
     // instructions of stage s+2 issued one per second-half MFMA (in program
     // order they must precede the LDS reads that follow them, which keeps them
     // spread out instead of in one burst after the barrier).
-    static_assert(PER_STAGE <= FN * FM, "one DMA instruction per second-half MFMA");
+    static_assert(PER_STAGE <= 2 * FN * FM, "at most two DMA instructions per second-half MFMA");
     int s = 0;
     for (; s + 2 < KT; ++s) {
         const int cur = s & 1;
@@ -368,7 +448,7 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_mfma_kernel(MfmaArgs p) 
         for (int a = 0; a < FN; ++a) {
 #pragma unroll
             for (int b = 0; b < FM; ++b) {
-                acc[a][b] = mfma_32x32x64_e4m3(fa[a], fb[b], acc[a][b]);
+                acc[a][b] = mma(fa[a], fb[b], acc[a][b], a, b, 0);
                 if (a == FN - 1) fb[b] = read_b(cur, 1, b);
             }
             fa[a] = read_a(cur, 1, a);
@@ -377,17 +457,20 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_mfma_kernel(MfmaArgs p) 
         wait_dma<PER_STAGE>(0);  // this wave's part of stage s+1 landed
         wait_lds_reads();        // ... and its reads of stage s are done
         block_barrier();
+        read_scales(cur ^ 1, nx_a, nx_b);
 #pragma unroll
         for (int a = 0; a < FN; ++a) {
 #pragma unroll
             for (int b = 0; b < FM; ++b) {
-                acc[a][b] = mfma_32x32x64_e4m3(fa[a], fb[b], acc[a][b]);
+                acc[a][b] = mma(fa[a], fb[b], acc[a][b], a, b, 1);
                 if (a * FM + b < PER_STAGE) issue_one(s + 2, cur, a * FM + b);
+                if (a * FM + b + FN * FM < PER_STAGE) issue_one(s + 2, cur, a * FM + b + FN * FM);
                 if (a == FN - 1) fb[b] = read_b(cur ^ 1, 0, b);
             }
             fa[a] = read_a(cur ^ 1, 0, a);
         }
-        interleave_mfma_reads<FN * FM, 2 * (FN + FM)>();
+        interleave_mfma_reads<FN * FM, 2 * (FN + FM) + SR>();
+        next_scales();
     }
     // The last two steps (nothing left to load).
     for (; s < KT; ++s) {
@@ -398,7 +481,7 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_mfma_kernel(MfmaArgs p) 
         for (int a = 0; a < FN; ++a) {
 #pragma unroll
             for (int b = 0; b < FM; ++b) {
-                acc[a][b] = mfma_32x32x64_e4m3(fa[a], fb[b], acc[a][b]);
+                acc[a][b] = mma(fa[a], fb[b], acc[a][b], a, b, 0);
                 if (a == FN - 1) fb[b] = read_b(cur, 1, b);
             }
             fa[a] = read_a(cur, 1, a);
@@ -408,6 +491,7 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_mfma_kernel(MfmaArgs p) 
             wait_dma<PER_STAGE>(0);
             wait_lds_reads();
             block_barrier();
+            read_scales(cur ^ 1, nx_a, nx_b);
         }
         // second K half of stage s; refill with the first half of stage s+1
         // (the last step re-reads its own slot, unused)
@@ -416,12 +500,13 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_mfma_kernel(MfmaArgs p) 
         for (int a = 0; a < FN; ++a) {
 #pragma unroll
             for (int b = 0; b < FM; ++b) {
-                acc[a][b] = mfma_32x32x64_e4m3(fa[a], fb[b], acc[a][b]);
+                acc[a][b] = mma(fa[a], fb[b], acc[a][b], a, b, 1);
                 if (a == FN - 1) fb[b] = read_b(nxt, 0, b);
             }
             fa[a] = read_a(nxt, 0, a);
         }
         interleave_mfma_reads<FN * FM, 2 * (FN + FM)>();
+        if (more) next_scales();
     }
 
     // ---- epilogue: y = bf16_rne(acc * (s_tok * s_ch)) ----------------------
@@ -526,6 +611,56 @@ hipError_t launch_gemm_mfma(const uint8_t* qa, int64_t lda, const float* s_tok, 
     if (e != hipSuccess) return e;
     const unsigned grid = (unsigned)p.tiles_m * (unsigned)p.tiles_n;
     hipLaunchKernelGGL((gemm_mfma_kernel<BN, BM, WN, WM, 4, false>), dim3(grid), dim3(64 * WN * WM), LDS, stream, p);
+    return hipGetLastError();
+}
+
+// Block-scale words from row-major [rows][chunks] to chunk-major
+// [chunks][rows] (one 32-bit word = a row's 4 exponent bytes of one 128-k
+// chunk).  Threads run along the rows, so the writes are contiguous.
+__global__ __launch_bounds__(256) void transpose_mx_scales(const uint32_t* __restrict__ in, int64_t rows, int chunks,
+                                                           uint32_t* __restrict__ out) {
+    const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (r >= rows) return;
+    for (int c = blockIdx.y; c < chunks; c += gridDim.y) out[(int64_t)c * rows + r] = in[r * chunks + c];
+}
+
+static void launch_transpose_scales(const uint8_t* in, int64_t rows, int64_t K, uint8_t* out, hipStream_t stream) {
+    const int chunks = (int)(K / 128);
+    const dim3 grid((unsigned)((rows + 255) / 256), (unsigned)(chunks < 64 ? chunks : 64));
+    hipLaunchKernelGGL(transpose_mx_scales, grid, dim3(256), 0, stream, reinterpret_cast<const uint32_t*>(in), rows,
+                       chunks, reinterpret_cast<uint32_t*>(out));
+}
+
+size_t gemm_mfma_mx_ws_bytes(int64_t M, int64_t N, int64_t K) {
+    auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+    return up((size_t)N * (size_t)(K / 32)) + up((size_t)M * (size_t)(K / 32));
+}
+
+hipError_t launch_gemm_mfma_mx(const uint8_t* qa, int64_t lda, const uint8_t* sa, const uint8_t* qw, int64_t ldw,
+                               const uint8_t* sw, uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K, void* ws,
+                               hipStream_t stream) {
+    if (M <= 0 || N <= 0) return hipSuccess;
+    uint8_t* sw_t = static_cast<uint8_t*>(ws);
+    uint8_t* sa_t = sw_t + (((size_t)N * (size_t)(K / 32) + 255) / 256 * 256);
+    if (K > 0) {
+        launch_transpose_scales(sw, N, K, sw_t, stream);
+        launch_transpose_scales(sa, M, K, sa_t, stream);
+    }
+    sa = sa_t;
+    sw = sw_t;
+    constexpr int BN = 256, BM = 256, WN = 2, WM = 2;
+    // ring + tile scales (ones) + block-scale ring
+    constexpr int LDS = 2 * (BN + BM) * kBK + 4 * (BN + BM) + 2 * 4 * (BN + BM);
+    MfmaArgs p{};
+    p.qa = qa; p.lda = lda; p.qw = qw; p.ldw = ldw; p.y = y; p.ldy = ldy;
+    p.M = (int)M; p.N = (int)N; p.K = (int)K;
+    p.tiles_m = (int)((M + BM - 1) / BM);
+    p.tiles_n = (int)((N + BN - 1) / BN);
+    p.mx = MxScales{sa, sw, (int)(K / 32)};
+    hipError_t e = FP8K_SET_LDS((gemm_mfma_kernel<BN, BM, WN, WM, 4, false, true>), LDS);
+    if (e != hipSuccess) return e;
+    const unsigned grid = (unsigned)p.tiles_m * (unsigned)p.tiles_n;
+    hipLaunchKernelGGL((gemm_mfma_kernel<BN, BM, WN, WM, 4, false, true>), dim3(grid), dim3(64 * WN * WM), LDS, stream, p);
     return hipGetLastError();
 }
 

@@ -34,12 +34,20 @@ __device__ __forceinline__ void issue_order_fence() { __builtin_amdgcn_sched_bar
 // [z * split_chunks, (z + 1) * split_chunks) and writes its fp32 sums to
 // part[z][m][n] (row stride N); skinny_splitk_reduce adds the splits in order
 // z = 0, 1, ... and applies the epilogue.
-template <int MT, int NT, int KW, int DEPTH>
+//
+// Block-scaled operands (MX = true): every 32 k of a row carry a power-of-two
+// scale (exponent byte) in mx.sa [M][K/32] and mx.sw [N][K/32]; the
+// hardware's block-scaled MFMA applies them, so there are no s_tok / s_ch
+// and y = bf16_rne(acc).  In this lane layout the scale that lane group g
+// supplies covers k [32g, 32g + 32) of the 128-byte chunk (measured on
+// gfx950), so each lane passes byte g of its row's 4 chunk scales.  K must be
+// a multiple of 128.
+template <int MT, int NT, int KW, int DEPTH, bool MX>
 __global__ __launch_bounds__(KW * 64) void gemm_skinny_kernel(
     const uint8_t* __restrict__ qa, int64_t lda, const float* __restrict__ s_tok,
     const uint8_t* __restrict__ qw, int64_t ldw, const float* __restrict__ s_ch,
     uint16_t* __restrict__ y, float* __restrict__ y32, int64_t ldy, int M, int N, int K, float* __restrict__ part,
-    int split_chunks) {
+    int split_chunks, MxScales mx) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int r16 = lane & 15;
@@ -61,6 +69,21 @@ __global__ __launch_bounds__(KW * 64) void gemm_skinny_kernel(
         const int m = 16 * i + r16;
         xrow[i] = qa + (int64_t)(m < M ? m : 0) * lda;
     }
+    constexpr int SD = MX ? DEPTH : 1;  // scale words in flight
+    const uint8_t* wsrow[NT];
+    const uint8_t* xsrow[MT];
+    if constexpr (MX) {
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            const int n = n0 + 16 * j + r16;
+            wsrow[j] = mx.sw + (int64_t)(n < N ? n : 0) * mx.nbk;
+        }
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+            const int m = 16 * i + r16;
+            xsrow[i] = mx.sa + (int64_t)(m < M ? m : 0) * mx.nbk;
+        }
+    }
 
     v4f acc[MT][NT];
 #pragma unroll
@@ -70,6 +93,7 @@ __global__ __launch_bounds__(KW * 64) void gemm_skinny_kernel(
 
     v4i wb[DEPTH][NT][2];
     v4i xb[DEPTH][MT][2];
+    uint32_t wsc[SD][NT], xsc[SD][MT];  // block scales of the chunk (MX)
     const v4i zero = v4i{0, 0, 0, 0};
 
     // Loads are issued raw and consumed DEPTH steps later; the operand
@@ -80,19 +104,26 @@ __global__ __launch_bounds__(KW * 64) void gemm_skinny_kernel(
     // would make the wave wait for everything issued before it).  Offsets past
     // K read the row's first bytes (K >= 16 whenever a step runs).  Rows past
     // N or M read row 0: they only feed output elements that are never stored.
-    auto load_step = [&](int s, v4i (&wd)[NT][2], v4i (&xd)[MT][2]) {
+    auto load_step = [&](int s, int d) {
         const int kb = (c0 + wave + KW * s) * 128;
         const int o0 = kb + 16 * g < K ? kb + 16 * g : 0;
         const int o1 = kb + 64 + 16 * g < K ? kb + 64 + 16 * g : 0;
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
-            wd[j][0] = load16(wrow[j] + o0);
-            wd[j][1] = load16(wrow[j] + o1);
+            wb[d][j][0] = load16(wrow[j] + o0);
+            wb[d][j][1] = load16(wrow[j] + o1);
         }
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
-            xd[i][0] = load16(xrow[i] + o0);
-            xd[i][1] = load16(xrow[i] + o1);
+            xb[d][i][0] = load16(xrow[i] + o0);
+            xb[d][i][1] = load16(xrow[i] + o1);
+        }
+        if constexpr (MX) {
+            const int so = kb >> 5;  // the chunk's 4 block scales (K % 128 == 0)
+#pragma unroll
+            for (int j = 0; j < NT; ++j) wsc[d][j] = *reinterpret_cast<const uint32_t*>(wsrow[j] + so);
+#pragma unroll
+            for (int i = 0; i < MT; ++i) xsc[d][i] = *reinterpret_cast<const uint32_t*>(xsrow[i] + so);
         }
     };
 
@@ -100,7 +131,7 @@ __global__ __launch_bounds__(KW * 64) void gemm_skinny_kernel(
         // (unconditional, so the compiler knows the return order exactly;
         // steps beyond the last repeat it and are never consumed)
 #pragma unroll
-        for (int d = 0; d < DEPTH; ++d) load_step(min(d, steps - 1), wb[d], xb[d]);
+        for (int d = 0; d < DEPTH; ++d) load_step(min(d, steps - 1), d);
         issue_order_fence();
         for (int s0 = 0; s0 < steps; s0 += DEPTH) {
 #pragma unroll
@@ -116,9 +147,16 @@ __global__ __launch_bounds__(KW * 64) void gemm_skinny_kernel(
                 for (int j = 0; j < NT; ++j) {
                     const v8i a = join(ok0 ? wb[d][j][0] : zero, ok1 ? wb[d][j][1] : zero);
 #pragma unroll
-                    for (int i = 0; i < MT; ++i) acc[i][j] = mfma_16x16x128_e4m3(a, xf[i], acc[i][j]);
+                    for (int i = 0; i < MT; ++i) {
+                        if constexpr (MX)
+                            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                                a, xf[i], acc[i][j], 0, 0, 0, (int)((wsc[d % SD][j] >> (8 * g)) & 0xFFu), 0,
+                                (int)((xsc[d % SD][i] >> (8 * g)) & 0xFFu));
+                        else
+                            acc[i][j] = mfma_16x16x128_e4m3(a, xf[i], acc[i][j]);
+                    }
                 }
-                if (s + DEPTH < steps) load_step(s + DEPTH, wb[d], xb[d]);
+                if (s + DEPTH < steps) load_step(s + DEPTH, d);
                 issue_order_fence();
             }
         }
@@ -146,6 +184,18 @@ __global__ __launch_bounds__(KW * 64) void gemm_skinny_kernel(
                 *reinterpret_cast<float4*>(pr + nb) = make_float4(sum[0], sum[1], sum[2], sum[3]);
             } else {
                 for (int v = 0; v < 4 && nb + v < N; ++v) pr[nb + v] = sum[v];
+            }
+            continue;
+        }
+        if constexpr (MX) {  // block scales already applied: y = bf16_rne(acc)
+            uint16_t* yr = y + (int64_t)m * ldy;
+            if (nb + 3 < N && (ldy & 3) == 0) {
+                uint2 o;
+                o.x = pack_bf16x2(sum[0], sum[1]);
+                o.y = pack_bf16x2(sum[2], sum[3]);
+                *reinterpret_cast<uint2*>(yr + nb) = o;
+            } else {
+                for (int v = 0; v < 4 && nb + v < N; ++v) yr[nb + v] = (uint16_t)bf16_rne_bits(sum[v]);
             }
             continue;
         }
@@ -361,7 +411,8 @@ __global__ __launch_bounds__(256) void skinny_splitk_reduce(const float* __restr
     const int nb = (int)(t - (int64_t)m * n4) * 4;
     const int64_t plane = (int64_t)M * N;
     const float* p = part + (int64_t)m * N + nb;
-    const float st = s_tok[m];
+    const bool unit = s_tok == nullptr;  // block-scaled sums: no epilogue scales
+    const float st = unit ? 1.0f : s_tok[m];
     if (nb + 3 < N && (N & 3) == 0 && (ldy & 3) == 0) {
         float4 a = *reinterpret_cast<const float4*>(p);
         for (int z = 1; z < splits; ++z) {
@@ -371,7 +422,7 @@ __global__ __launch_bounds__(256) void skinny_splitk_reduce(const float* __restr
             a.z += b.z;
             a.w += b.w;
         }
-        const float4 sc = *reinterpret_cast<const float4*>(s_ch + nb);
+        const float4 sc = unit ? make_float4(1.0f, 1.0f, 1.0f, 1.0f) : *reinterpret_cast<const float4*>(s_ch + nb);
         if (y32 != nullptr) {
             *reinterpret_cast<float4*>(y32 + (int64_t)m * ldy + nb) =
                 make_float4(a.x * (st * sc.x), a.y * (st * sc.y), a.z * (st * sc.z), a.w * (st * sc.w));
@@ -386,32 +437,38 @@ __global__ __launch_bounds__(256) void skinny_splitk_reduce(const float* __restr
         for (int v = 0; v < 4 && nb + v < N; ++v) {
             float a = p[v];
             for (int z = 1; z < splits; ++z) a += p[z * plane + v];
+            const float sc = unit ? 1.0f : s_ch[nb + v];
             if (y32 != nullptr)
-                y32[(int64_t)m * ldy + nb + v] = a * (st * s_ch[nb + v]);
+                y32[(int64_t)m * ldy + nb + v] = a * (st * sc);
             else
-                y[(int64_t)m * ldy + nb + v] = (uint16_t)bf16_rne_bits(a * (st * s_ch[nb + v]));
+                y[(int64_t)m * ldy + nb + v] = (uint16_t)bf16_rne_bits(a * (st * sc));
         }
     }
 }
 
-template <int MT, int NT, int KW>
+template <int MT, int NT, int KW, bool MX>
 static void launch_cfg(dim3 grid, hipStream_t stream, const uint8_t* qa, int64_t lda, const float* s_tok,
                        const uint8_t* qw, int64_t ldw, const float* s_ch, uint16_t* y, float* y32, int64_t ldy, int M,
-                       int N, int K, float* part, int split_chunks) {
-    constexpr int DEPTH = (MT * NT <= 2) ? 4 : 2;
-    hipLaunchKernelGGL((gemm_skinny_kernel<MT, NT, KW, DEPTH>), grid, dim3(KW * 64), 0, stream, qa, lda, s_tok, qw,
-                       ldw, s_ch, y, y32, ldy, M, N, K, part, split_chunks);
+                       int N, int K, float* part, int split_chunks, MxScales mx) {
+    // The block-scaled MFMA keeps its operands in VGPRs (the plain one also
+    // reads AGPRs), so the MX kernels keep fewer steps in flight to stay
+    // within the register file without spills (checked in the compiler's
+    // register report for every instantiation).
+    constexpr int DEPTH = MX ? (MT * NT == 1 ? 4 : ((NT == 8 ? MT == 1 : MT * NT <= 6) ? 2 : 1))
+                             : ((MT * NT <= 2) ? 4 : 2);
+    hipLaunchKernelGGL((gemm_skinny_kernel<MT, NT, KW, DEPTH, MX>), grid, dim3(KW * 64), 0, stream, qa, lda, s_tok,
+                       qw, ldw, s_ch, y, y32, ldy, M, N, K, part, split_chunks, mx);
 }
 
-template <int MT>
+template <int MT, bool MX>
 static void launch_mt(int nt, dim3 grid, hipStream_t stream, const uint8_t* qa, int64_t lda, const float* s_tok,
                       const uint8_t* qw, int64_t ldw, const float* s_ch, uint16_t* y, float* y32, int64_t ldy, int M,
-                      int N, int K, float* part, int split_chunks) {
+                      int N, int K, float* part, int split_chunks, MxScales mx) {
     switch (nt) {
-        case 8: launch_cfg<MT, 8, 4>(grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, y32, ldy, M, N, K, part, split_chunks); break;
-        case 4: launch_cfg<MT, 4, 8>(grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, y32, ldy, M, N, K, part, split_chunks); break;
-        case 2: launch_cfg<MT, 2, 8>(grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, y32, ldy, M, N, K, part, split_chunks); break;
-        default: launch_cfg<MT, 1, 8>(grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, y32, ldy, M, N, K, part, split_chunks); break;
+        case 8: launch_cfg<MT, 8, 4, MX>(grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, y32, ldy, M, N, K, part, split_chunks, mx); break;
+        case 4: launch_cfg<MT, 4, 8, MX>(grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, y32, ldy, M, N, K, part, split_chunks, mx); break;
+        case 2: launch_cfg<MT, 2, 8, MX>(grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, y32, ldy, M, N, K, part, split_chunks, mx); break;
+        default: launch_cfg<MT, 1, 8, MX>(grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, y32, ldy, M, N, K, part, split_chunks, mx); break;
     }
 }
 
@@ -472,26 +529,43 @@ size_t gemm_skinny_ws_bytes(int64_t M, int64_t N, int64_t K) {
     return p.splits > 1 ? (size_t)p.splits * (size_t)M * (size_t)N * sizeof(float) : 0;
 }
 
-hipError_t launch_gemm_skinny(const uint8_t* qa, int64_t lda, const float* s_tok, const uint8_t* qw,
-                              int64_t ldw, const float* s_ch, uint16_t* y, float* y32, int64_t ldy, int64_t M, int64_t N,
-                              int64_t K, void* ws, hipStream_t stream) {
+template <bool MX>
+static hipError_t launch_skinny_any(const uint8_t* qa, int64_t lda, const float* s_tok, const uint8_t* qw,
+                                    int64_t ldw, const float* s_ch, uint16_t* y, float* y32, int64_t ldy, int64_t M,
+                                    int64_t N, int64_t K, void* ws, MxScales mx, hipStream_t stream) {
     if (M <= 0 || N <= 0) return hipSuccess;
-    const SkinnyPlan p = skinny_plan(M, N, K);
+    SkinnyPlan p = skinny_plan(M, N, K);
+    // MX: 4 activation tiles with nt = 4 (8 waves, 256 VGPRs each) would
+    // spill; take nt = 8 (4 waves) there (same splits: none on this branch)
+    if (MX && p.mt == 4 && p.nt == 4) p.nt = 8;
     float* part = p.splits > 1 ? static_cast<float*>(ws) : nullptr;
     const dim3 grid((unsigned)((N + 16 * p.nt - 1) / (16 * p.nt)), 1, (unsigned)p.splits);
     const int m = (int)M, n = (int)N, k = (int)K;
     switch (p.mt) {
-        case 1: launch_mt<1>(p.nt, grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, y32, ldy, m, n, k, part, p.split_chunks); break;
-        case 2: launch_mt<2>(p.nt, grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, y32, ldy, m, n, k, part, p.split_chunks); break;
-        case 3: launch_mt<3>(p.nt, grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, y32, ldy, m, n, k, part, p.split_chunks); break;
-        default: launch_mt<4>(p.nt, grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, y32, ldy, m, n, k, part, p.split_chunks); break;
+        case 1: launch_mt<1, MX>(p.nt, grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, y32, ldy, m, n, k, part, p.split_chunks, mx); break;
+        case 2: launch_mt<2, MX>(p.nt, grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, y32, ldy, m, n, k, part, p.split_chunks, mx); break;
+        case 3: launch_mt<3, MX>(p.nt, grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, y32, ldy, m, n, k, part, p.split_chunks, mx); break;
+        default: launch_mt<4, MX>(p.nt, grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, y32, ldy, m, n, k, part, p.split_chunks, mx); break;
     }
     if (part != nullptr) {
         const int64_t threads = M * ((N + 3) / 4);
         hipLaunchKernelGGL(skinny_splitk_reduce, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, part,
-                           p.splits, m, n, s_tok, s_ch, y, y32, ldy);
+                           p.splits, m, n, MX ? nullptr : s_tok, MX ? nullptr : s_ch, y, y32, ldy);
     }
     return hipGetLastError();
+}
+
+hipError_t launch_gemm_skinny(const uint8_t* qa, int64_t lda, const float* s_tok, const uint8_t* qw,
+                              int64_t ldw, const float* s_ch, uint16_t* y, float* y32, int64_t ldy, int64_t M, int64_t N,
+                              int64_t K, void* ws, hipStream_t stream) {
+    return launch_skinny_any<false>(qa, lda, s_tok, qw, ldw, s_ch, y, y32, ldy, M, N, K, ws, MxScales{}, stream);
+}
+
+hipError_t launch_gemm_skinny_mx(const uint8_t* qa, int64_t lda, const uint8_t* sa, const uint8_t* qw, int64_t ldw,
+                                 const uint8_t* sw, uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K, void* ws,
+                                 hipStream_t stream) {
+    return launch_skinny_any<true>(qa, lda, nullptr, qw, ldw, nullptr, y, nullptr, ldy, M, N, K, ws,
+                                   MxScales{sa, sw, (int)(K / 32)}, stream);
 }
 
 // The one-kernel path pays for every workgroup reading all of x (fp32) from

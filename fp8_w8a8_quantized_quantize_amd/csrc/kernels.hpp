@@ -47,6 +47,19 @@ hipError_t launch_kv_dequantize_paged(const uint8_t* cache, int64_t num_slots, c
 // The dense GEMM launchers write BF16 y, or, when y32 is not null, the fp32
 // value acc * (s_tok * s_ch) before rounding to y32 (same row stride ldy).
 
+// Block-scaled quantization (block_scale.hip): K % 32 == 0; scales u8
+// [rows][K / 32] (exponent bytes, 2^(c - 127)).
+hipError_t launch_quantize_mx(const float* x, int64_t ldx, uint8_t* q, int64_t ldq, uint8_t* scales, int64_t rows,
+                              int64_t K, hipStream_t stream);
+
+// Block ("MX") scales of both GEMM operands: exponent bytes, 2^(c - 127),
+// one per 32 k of a row; sa [M][nbk], sw [N][nbk], nbk = K / 32.
+struct MxScales {
+    const uint8_t* sa;
+    const uint8_t* sw;
+    int nbk;
+};
+
 // Largest M the skinny (decode) kernel takes.
 constexpr int64_t kSkinnyMaxM = 64;
 
@@ -62,6 +75,20 @@ size_t gemm_skinny_ws_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_skinny(const uint8_t* qa, int64_t lda, const float* s_tok, const uint8_t* qw,
                               int64_t ldw, const float* s_ch, uint16_t* y, float* y32, int64_t ldy, int64_t M, int64_t N,
                               int64_t K, void* ws, hipStream_t stream);
+
+// Block-scaled skinny GEMM (K % 128 == 0): y = bf16_rne(sum over blocks of
+// 2^(sa + sw - 254) * block dot); same plan and workspace as above.
+hipError_t launch_gemm_skinny_mx(const uint8_t* qa, int64_t lda, const uint8_t* sa, const uint8_t* qw, int64_t ldw,
+                                 const uint8_t* sw, uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K, void* ws,
+                                 hipStream_t stream);
+
+// Block-scaled MFMA GEMM for M > kSkinnyMaxM, K % 128 == 0 (gemm_mfma.hip).
+// ws (gemm_mfma_mx_ws_bytes, 16-byte aligned) receives the scales in
+// chunk-major order before the GEMM runs.
+size_t gemm_mfma_mx_ws_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_mfma_mx(const uint8_t* qa, int64_t lda, const uint8_t* sa, const uint8_t* qw, int64_t ldw,
+                               const uint8_t* sw, uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K, void* ws,
+                               hipStream_t stream);
 
 // Quantize + skinny GEMM in one kernel, for M <= kSkinnyFusedMaxM rows whose
 // codes fit in kSkinnyFusedLds bytes of LDS and N <= 8192 (gemm_skinny.hip).  qa_out and
