@@ -478,7 +478,7 @@ def bench_mx(args, w, dev, steps, warmup, graph, log):
     wcopies = [(wq, ws_)] + [(wq.clone(), ws_.clone()) for _ in range(copies - 1)]
     xd = torch.from_numpy(x).to(dev)
     qa = torch.empty((M, K), dtype=torch.uint8, device=dev)
-    sa = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
+    sa = torch.empty((K // 128, M, 4), dtype=torch.uint8, device=dev)
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     ws = torch.empty(max(1, fp8.fp8_mx_workspace_bytes(M, N, K)), dtype=torch.uint8, device=dev)
 

@@ -232,34 +232,38 @@ def fp8_mx_workspace_bytes(M, N, K):
 
 
 def fp8_quantize_mx(x, q=None, scales=None, stream=None):
-    """Block-scaled E4M3 quantization of fp32 x [M, K] (K % 32 == 0) ->
-    (q uint8 [M, K], scales uint8 [M, K/32] exponent bytes)."""
+    """Block-scaled E4M3 quantization of fp32 x [M, K] (K % 128 == 0) ->
+    (q uint8 [M, K], scales uint8 [K/128, M, 4] chunk-major exponent bytes)."""
     torch = _torch()
     M, K, ldx = _rows(x, torch.float32, "x")
     if q is None:
         q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
     if scales is None:
-        scales = torch.empty((M, K // 32), dtype=torch.uint8, device=x.device)
+        scales = torch.empty((K // 128, M, 4), dtype=torch.uint8, device=x.device)
     _, _, ldq = _rows(q, torch.uint8, "q")
-    if not isinstance(scales, torch.Tensor) or scales.dtype != torch.uint8 or not scales.is_cuda \
-            or not scales.is_contiguous() or tuple(scales.shape) != (M, K // 32):
-        raise TypeError("scales: expected a contiguous uint8 CUDA tensor [M, K/32]")
+    _mx_scales(scales, "scales", M, K)
     _check("fp8_quantize_mx", lib().fp8_quantize_mx(_ptr(x), M, K, ldx, _ptr(q), ldq, _ptr(scales), _stream(stream)))
     return q, scales
 
 
+def _mx_scales(t, name, rows, K):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.uint8 or not t.is_cuda or not t.is_contiguous() \
+            or tuple(t.shape) != (K // 128, rows, 4):
+        raise TypeError(f"{name}: expected a contiguous uint8 CUDA tensor [K/128, {rows}, 4]")
+
+
 def fp8_gemm_mx(qa, sa, qw, sw, y=None, ws=None, stream=None):
-    """y = bf16(sum over 32-blocks of 2^(sa + sw - 254) * block dot) for block-scaled
-    E4M3 operands qa [M, K], qw [N, K] with exponent bytes sa [M, K/32], sw [N, K/32]."""
+    """y = bf16(sum over 32-blocks of 2^(ea + ew - 254) * block dot) for block-scaled
+    E4M3 operands qa [M, K], qw [N, K] with chunk-major exponent bytes sa [K/128, M, 4],
+    sw [K/128, N, 4]."""
     torch = _torch()
     M, K, lda = _rows(qa, torch.uint8, "qa")
     N, K2, ldw = _rows(qw, torch.uint8, "qw")
     if K2 != K:
         raise ValueError("qa and qw disagree on K")
-    for t, name, rows in ((sa, "sa", M), (sw, "sw", N)):
-        if not isinstance(t, torch.Tensor) or t.dtype != torch.uint8 or not t.is_cuda or not t.is_contiguous() \
-                or tuple(t.shape) != (rows, K // 32):
-            raise TypeError(f"{name}: expected a contiguous uint8 CUDA tensor [{rows}, K/32]")
+    _mx_scales(sa, "sa", M, K)
+    _mx_scales(sw, "sw", N, K)
     if y is None:
         y = torch.empty((M, N), dtype=torch.bfloat16, device=qa.device)
     _, _, ldy = _rows(y, torch.bfloat16, "y")

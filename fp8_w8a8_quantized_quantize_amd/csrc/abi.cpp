@@ -203,20 +203,17 @@ fp8_status_t fp8_calibrate_percentile(const float* x, int64_t n, int64_t num, in
 fp8_status_t fp8_quantize_mx(const float* x, int64_t rows, int64_t K, int64_t ldx, uint8_t* q, int64_t ldq,
                              uint8_t* scales, hipStream_t stream) {
     FP8_TRY(check_dims(rows, 1, K));
-    if (K % 32 != 0) return FP8_ERR_UNSUPPORTED;
+    if (K % 128 != 0) return FP8_ERR_UNSUPPORTED;
     FP8_TRY(check_matrix(x, rows, K, ldx, 4));
     FP8_TRY(check_matrix(q, rows, K, ldq, 1));
-    FP8_TRY(check_matrix(scales, rows, K / 32, K / 32, 1, true));
+    FP8_TRY(check_matrix(scales, K / 128, 4 * rows, 4 * rows, 1, true));
     if (rows == 0 || K == 0) return FP8_OK;
     return from_hip(fp8k::launch_quantize_mx(x, ldx, q, ldq, scales, rows, K, stream));
 }
 
 // The block-scaled GEMM's workspace: the skinny kernel's split-K partial
-// sums (M <= 64), or the chunk-major copies of both scale matrices (M > 64).
-size_t mx_ws_bytes(int64_t M, int64_t N, int64_t K) {
-    if (M <= 0 || N <= 0) return 0;
-    return M <= fp8k::kSkinnyMaxM ? gemm_ws_bytes(M, N, K) : fp8k::gemm_mfma_mx_ws_bytes(M, N, K);
-}
+// sums (M <= 64); none for the MFMA kernel.
+static size_t mx_ws_bytes(int64_t M, int64_t N, int64_t K) { return gemm_ws_bytes(M, N, K); }
 
 size_t fp8_mx_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     if (check_dims(M, N, K) != FP8_OK || K % 128 != 0) return SIZE_MAX;
@@ -244,7 +241,7 @@ fp8_status_t fp8_gemm_mx(const uint8_t* qa, int64_t lda, const uint8_t* sa, cons
     if (M == 0 || N == 0) return FP8_OK;
     if (M <= fp8k::kSkinnyMaxM)
         return from_hip(fp8k::launch_gemm_skinny_mx(qa, lda, sa, qw, ldw, sw, y, ldy, M, N, K, ws, stream));
-    return from_hip(fp8k::launch_gemm_mfma_mx(qa, lda, sa, qw, ldw, sw, y, ldy, M, N, K, ws, stream));
+    return from_hip(fp8k::launch_gemm_mfma_mx(qa, lda, sa, qw, ldw, sw, y, ldy, M, N, K, stream));
 }
 
 size_t fp8_kv_scales_workspace_bytes(int64_t T, int64_t C) {

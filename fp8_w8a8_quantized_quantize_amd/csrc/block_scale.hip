@@ -10,6 +10,11 @@
 // smallest integer with 2^e >= v, so every |x| / 2^e <= 448 and nothing is
 // clipped; codes are E4M3(x * 2^-e), rounded to nearest even.
 //
+// Scales are stored chunk-major: for each 128-element chunk of K, one 32-bit
+// word per row holding the exponent bytes of its 4 blocks (word [chunk][row],
+// byte j = block 4 * chunk + j), the order in which the GEMM kernels fetch
+// them (a chunk's words for consecutive rows are contiguous).
+//
 // One float4 per thread; the 8 threads of a block reduce their maxima with
 // three butterfly steps.  The stream is read once (nontemporal loads for
 // large inputs, as in the per-token quantizer).
@@ -34,8 +39,8 @@ __device__ __forceinline__ float4 mx_load(const float4* p, bool nt) {
 template <bool NT>
 __global__ __launch_bounds__(kMxThreads) void quantize_mx_kernel(const float* __restrict__ x, int64_t ldx,
                                                                   uint8_t* __restrict__ q, int64_t ldq,
-                                                                  uint8_t* __restrict__ sc, int64_t K4,
-                                                                  int64_t total) {
+                                                                  uint8_t* __restrict__ sc, int64_t rows,
+                                                                  int64_t K4, int64_t total) {
     for (int64_t i = (int64_t)blockIdx.x * kMxThreads + threadIdx.x; i < total;
          i += (int64_t)gridDim.x * kMxThreads) {
         const int64_t row = i / K4;
@@ -51,7 +56,8 @@ __global__ __launch_bounds__(kMxThreads) void quantize_mx_kernel(const float* __
         const int e = (int)(bits >> 23) - 127 + ((bits & 0x7FFFFFu) != 0u);
         const float inv = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e, e in [-39, 120]
         *reinterpret_cast<uint32_t*>(q + row * ldq + 4 * c4) = cvt4_e4m3(v.x * inv, v.y * inv, v.z * inv, v.w * inv);
-        if ((c4 & 7) == 0) sc[row * (K4 >> 3) + (c4 >> 3)] = (uint8_t)(e + 127);
+        // chunk-major: byte j of word [chunk][row] is block 4 * chunk + j
+        if ((c4 & 7) == 0) sc[((c4 >> 5) * rows + row) * 4 + ((c4 >> 3) & 3)] = (uint8_t)(e + 127);
     }
 }
 
@@ -64,10 +70,10 @@ hipError_t launch_quantize_mx(const float* x, int64_t ldx, uint8_t* q, int64_t l
     if (blocks > (1 << 20)) blocks = 1 << 20;
     if (rows >= 512)
         hipLaunchKernelGGL(quantize_mx_kernel<true>, dim3((unsigned)blocks), dim3(kMxThreads), 0, stream, x, ldx, q,
-                           ldq, scales, K4, total);
+                           ldq, scales, rows, K4, total);
     else
         hipLaunchKernelGGL(quantize_mx_kernel<false>, dim3((unsigned)blocks), dim3(kMxThreads), 0, stream, x, ldx, q,
-                           ldq, scales, K4, total);
+                           ldq, scales, rows, K4, total);
     return hipGetLastError();
 }
 

@@ -207,10 +207,10 @@ __device__ void find_expert_tile(const MfmaArgs& p, int b, int* sh) {
 // DMA instructions per wave into a ring of their own); a lane reads its
 // fragment rows' words for stage s + 1 after the barrier of step s and passes
 // byte 2h + g for K half h; the tile scales of the epilogue are 1.  The
-// scales arrive chunk-major (word [kt][row], see transpose_mx_scales), so a
-// stage's words for consecutive rows are contiguous: the natural [row][kt]
-// order made every lane of a scale DMA touch its own cache line (measured:
-// 23 % slower on 8192^3).
+// scales are chunk-major (word [kt][row]), so a stage's words for
+// consecutive rows are contiguous: a row-major [row][kt] order made every
+// lane of a scale DMA touch its own cache line (measured: 23 % slower on
+// 8192^3).
 template <int BN, int BM, int WN, int WM, int GROUP_M, bool GROUPED, bool MX = false>
 __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_mfma_kernel(MfmaArgs p) {
     static_assert(!(MX && GROUPED), "block scales: dense GEMM only");
@@ -614,40 +614,10 @@ hipError_t launch_gemm_mfma(const uint8_t* qa, int64_t lda, const float* s_tok, 
     return hipGetLastError();
 }
 
-// Block-scale words from row-major [rows][chunks] to chunk-major
-// [chunks][rows] (one 32-bit word = a row's 4 exponent bytes of one 128-k
-// chunk).  Threads run along the rows, so the writes are contiguous.
-__global__ __launch_bounds__(256) void transpose_mx_scales(const uint32_t* __restrict__ in, int64_t rows, int chunks,
-                                                           uint32_t* __restrict__ out) {
-    const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (r >= rows) return;
-    for (int c = blockIdx.y; c < chunks; c += gridDim.y) out[(int64_t)c * rows + r] = in[r * chunks + c];
-}
-
-static void launch_transpose_scales(const uint8_t* in, int64_t rows, int64_t K, uint8_t* out, hipStream_t stream) {
-    const int chunks = (int)(K / 128);
-    const dim3 grid((unsigned)((rows + 255) / 256), (unsigned)(chunks < 64 ? chunks : 64));
-    hipLaunchKernelGGL(transpose_mx_scales, grid, dim3(256), 0, stream, reinterpret_cast<const uint32_t*>(in), rows,
-                       chunks, reinterpret_cast<uint32_t*>(out));
-}
-
-size_t gemm_mfma_mx_ws_bytes(int64_t M, int64_t N, int64_t K) {
-    auto up = [](size_t v) { return (v + 255) / 256 * 256; };
-    return up((size_t)N * (size_t)(K / 32)) + up((size_t)M * (size_t)(K / 32));
-}
-
 hipError_t launch_gemm_mfma_mx(const uint8_t* qa, int64_t lda, const uint8_t* sa, const uint8_t* qw, int64_t ldw,
-                               const uint8_t* sw, uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K, void* ws,
+                               const uint8_t* sw, uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K,
                                hipStream_t stream) {
     if (M <= 0 || N <= 0) return hipSuccess;
-    uint8_t* sw_t = static_cast<uint8_t*>(ws);
-    uint8_t* sa_t = sw_t + (((size_t)N * (size_t)(K / 32) + 255) / 256 * 256);
-    if (K > 0) {
-        launch_transpose_scales(sw, N, K, sw_t, stream);
-        launch_transpose_scales(sa, M, K, sa_t, stream);
-    }
-    sa = sa_t;
-    sw = sw_t;
     constexpr int BN = 256, BM = 256, WN = 2, WM = 2;
     // ring + tile scales (ones) + block-scale ring
     constexpr int LDS = 2 * (BN + BM) * kBK + 4 * (BN + BM) + 2 * 4 * (BN + BM);
@@ -656,7 +626,7 @@ hipError_t launch_gemm_mfma_mx(const uint8_t* qa, int64_t lda, const uint8_t* sa
     p.M = (int)M; p.N = (int)N; p.K = (int)K;
     p.tiles_m = (int)((M + BM - 1) / BM);
     p.tiles_n = (int)((N + BN - 1) / BN);
-    p.mx = MxScales{sa, sw, (int)(K / 32)};
+    p.mx = MxScales{sa, sw};
     hipError_t e = FP8K_SET_LDS((gemm_mfma_kernel<BN, BM, WN, WM, 4, false, true>), LDS);
     if (e != hipSuccess) return e;
     const unsigned grid = (unsigned)p.tiles_m * (unsigned)p.tiles_n;

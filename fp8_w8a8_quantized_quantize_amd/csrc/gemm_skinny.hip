@@ -36,12 +36,12 @@ __device__ __forceinline__ void issue_order_fence() { __builtin_amdgcn_sched_bar
 // z = 0, 1, ... and applies the epilogue.
 //
 // Block-scaled operands (MX = true): every 32 k of a row carry a power-of-two
-// scale (exponent byte) in mx.sa [M][K/32] and mx.sw [N][K/32]; the
-// hardware's block-scaled MFMA applies them, so there are no s_tok / s_ch
-// and y = bf16_rne(acc).  In this lane layout the scale that lane group g
-// supplies covers k [32g, 32g + 32) of the 128-byte chunk (measured on
-// gfx950), so each lane passes byte g of its row's 4 chunk scales.  K must be
-// a multiple of 128.
+// scale (exponent byte), chunk-major in mx.sa / mx.sw (32-bit word
+// [chunk][row]); the hardware's block-scaled MFMA applies them, so there are
+// no s_tok / s_ch and y = bf16_rne(acc).  In this lane layout the scale that
+// lane group g supplies covers k [32g, 32g + 32) of the 128-byte chunk
+// (measured on gfx950), so each lane passes byte g of its row's chunk word.
+// K must be a multiple of 128.
 template <int MT, int NT, int KW, int DEPTH, bool MX>
 __global__ __launch_bounds__(KW * 64) void gemm_skinny_kernel(
     const uint8_t* __restrict__ qa, int64_t lda, const float* __restrict__ s_tok,
@@ -76,12 +76,12 @@ __global__ __launch_bounds__(KW * 64) void gemm_skinny_kernel(
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
             const int n = n0 + 16 * j + r16;
-            wsrow[j] = mx.sw + (int64_t)(n < N ? n : 0) * mx.nbk;
+            wsrow[j] = mx.sw + 4 * (int64_t)(n < N ? n : 0);
         }
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
             const int m = 16 * i + r16;
-            xsrow[i] = mx.sa + (int64_t)(m < M ? m : 0) * mx.nbk;
+            xsrow[i] = mx.sa + 4 * (int64_t)(m < M ? m : 0);
         }
     }
 
@@ -119,11 +119,13 @@ __global__ __launch_bounds__(KW * 64) void gemm_skinny_kernel(
             xb[d][i][1] = load16(xrow[i] + o1);
         }
         if constexpr (MX) {
-            const int so = kb >> 5;  // the chunk's 4 block scales (K % 128 == 0)
+            const int64_t chunk = kb >> 7;  // the chunk's word of 4 block scales (K % 128 == 0)
 #pragma unroll
-            for (int j = 0; j < NT; ++j) wsc[d][j] = *reinterpret_cast<const uint32_t*>(wsrow[j] + so);
+            for (int j = 0; j < NT; ++j)
+                wsc[d][j] = *reinterpret_cast<const uint32_t*>(wsrow[j] + chunk * 4 * (int64_t)N);
 #pragma unroll
-            for (int i = 0; i < MT; ++i) xsc[d][i] = *reinterpret_cast<const uint32_t*>(xsrow[i] + so);
+            for (int i = 0; i < MT; ++i)
+                xsc[d][i] = *reinterpret_cast<const uint32_t*>(xsrow[i] + chunk * 4 * (int64_t)M);
         }
     };
 
@@ -565,7 +567,7 @@ hipError_t launch_gemm_skinny_mx(const uint8_t* qa, int64_t lda, const uint8_t* 
                                  const uint8_t* sw, uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K, void* ws,
                                  hipStream_t stream) {
     return launch_skinny_any<true>(qa, lda, nullptr, qw, ldw, nullptr, y, nullptr, ldy, M, N, K, ws,
-                                   MxScales{sa, sw, (int)(K / 32)}, stream);
+                                   MxScales{sa, sw}, stream);
 }
 
 // The one-kernel path pays for every workgroup reading all of x (fp32) from

@@ -47,17 +47,17 @@ hipError_t launch_kv_dequantize_paged(const uint8_t* cache, int64_t num_slots, c
 // The dense GEMM launchers write BF16 y, or, when y32 is not null, the fp32
 // value acc * (s_tok * s_ch) before rounding to y32 (same row stride ldy).
 
-// Block-scaled quantization (block_scale.hip): K % 32 == 0; scales u8
-// [rows][K / 32] (exponent bytes, 2^(c - 127)).
+// Block-scaled quantization (block_scale.hip): K % 128 == 0; scales are
+// chunk-major exponent bytes: word [K / 128][rows], byte j = block 4c + j.
 hipError_t launch_quantize_mx(const float* x, int64_t ldx, uint8_t* q, int64_t ldq, uint8_t* scales, int64_t rows,
                               int64_t K, hipStream_t stream);
 
 // Block ("MX") scales of both GEMM operands: exponent bytes, 2^(c - 127),
-// one per 32 k of a row; sa [M][nbk], sw [N][nbk], nbk = K / 32.
+// one per 32 k of a row, chunk-major: 32-bit word [K / 128][rows] holds a
+// row's 4 bytes of one 128-k chunk.  sa covers M rows, sw N rows.
 struct MxScales {
     const uint8_t* sa;
     const uint8_t* sw;
-    int nbk;
 };
 
 // Largest M the skinny (decode) kernel takes.
@@ -83,11 +83,8 @@ hipError_t launch_gemm_skinny_mx(const uint8_t* qa, int64_t lda, const uint8_t* 
                                  hipStream_t stream);
 
 // Block-scaled MFMA GEMM for M > kSkinnyMaxM, K % 128 == 0 (gemm_mfma.hip).
-// ws (gemm_mfma_mx_ws_bytes, 16-byte aligned) receives the scales in
-// chunk-major order before the GEMM runs.
-size_t gemm_mfma_mx_ws_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_mfma_mx(const uint8_t* qa, int64_t lda, const uint8_t* sa, const uint8_t* qw, int64_t ldw,
-                               const uint8_t* sw, uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K, void* ws,
+                               const uint8_t* sw, uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K,
                                hipStream_t stream);
 
 // Quantize + skinny GEMM in one kernel, for M <= kSkinnyFusedMaxM rows whose

@@ -222,15 +222,17 @@ size_t fp8_grouped_workspace_bytes(int64_t T, int64_t R, int64_t E, int64_t N, i
 /*
  * Block-scaled ("MX") quantization (per-group/block scales: DeepSeek V4 950
  * page, §2.4 and §4.2; MXFP8 block scaling: FP8 deployment page, §7.1):
- * every 32 consecutive elements of a row share a power-of-two scale, kept as
- * its exponent byte c (scale 2^(c - 127)):
- *   v        = max(fl32(max_{k in block} |x[r,k]| / 448), 1e-12f)
- *   e        = the smallest integer with 2^e >= v     (so nothing clips)
- *   scales[r, b] = e + 127            (u8 [rows, K/32], unit-stride rows)
- *   q[r,k]   = E4M3 code of x[r,k] * 2^-e, RNE
- * x: fp32 [rows, K], stride ldx; q: u8 [rows, K], stride ldq.  K must be a
- * multiple of 32 (else FP8_ERR_UNSUPPORTED); the other conventions as for
- * fp8_quantize_per_token.  No workspace.
+ * every 32 consecutive elements of a row (block b = k / 32) share a
+ * power-of-two scale, kept as its exponent byte c (scale 2^(c - 127)):
+ *   v      = max(fl32(max_{k in block} |x[r,k]| / 448), 1e-12f)
+ *   e      = the smallest integer with 2^e >= v     (so nothing clips)
+ *   q[r,k] = E4M3 code of x[r,k] * 2^-e, RNE
+ * x: fp32 [rows, K], stride ldx; q: u8 [rows, K], stride ldq.
+ * Scale layout (chunk-major, the order the GEMM kernels fetch it): u8
+ * [K/128][rows][4]; byte j of row r in chunk c is the exponent byte of block
+ * 4c + j, i.e. scales[(c * rows + r) * 4 + j] = e(r, 4c + j) + 127.
+ * K must be a multiple of 128 (else FP8_ERR_UNSUPPORTED); the other
+ * conventions as for fp8_quantize_per_token.  No workspace.
  */
 fp8_status_t fp8_quantize_mx(const float* x, int64_t rows, int64_t K, int64_t ldx, uint8_t* q, int64_t ldq,
                              uint8_t* scales, hipStream_t stream);
@@ -239,15 +241,15 @@ fp8_status_t fp8_quantize_mx(const float* x, int64_t rows, int64_t K, int64_t ld
  * Block-scaled FP8 GEMM with BF16 output (block scales applied inside the K
  * loop by gfx950's block-scaled MFMA; FP32 accumulation, DeepSeek V4 950
  * page, §2.3):
- *   y[m,n] = bf16_rne( sum_b 2^(sa[m,b] + sw[n,b] - 254)
+ *   y[m,n] = bf16_rne( sum_b 2^(ea(m,b) + ew(n,b) - 254)
  *                          * sum_{k in block b} e4m3(qa[m,k]) * e4m3(qw[n,k]) )
- * qa u8 [M, K] (lda), qw u8 [N, K] (ldw), sa u8 [M, K/32], sw u8 [N, K/32]
- * (exponent bytes as written by fp8_quantize_mx, unit-stride rows, 4-byte
- * aligned), y bf16 [M, N] (ldy).  K must be a multiple of 128 (K == 0
- * gives y = 0).  ws: at least fp8_mx_workspace_bytes(M, N, K) bytes,
- * 16-byte aligned (decode shapes that split K keep fp32 partial sums there;
- * M > 64 keeps chunk-major copies of sa and sw there, (M + N) * K / 32 bytes
- * rounded up; may be NULL when that is 0; contents on entry do not matter).
+ * qa u8 [M, K] (lda), qw u8 [N, K] (ldw); sa u8 [K/128][M][4] and sw u8
+ * [K/128][N][4] hold the exponent bytes ea, ew in the chunk-major layout
+ * fp8_quantize_mx writes (4-byte aligned); y bf16 [M, N] (ldy).  K must be
+ * a multiple of 128 (K == 0 gives y = 0).  ws: at least
+ * fp8_mx_workspace_bytes(M, N, K) bytes, 16-byte aligned (decode shapes that
+ * split K keep fp32 partial sums there; may be NULL when that is 0; contents
+ * on entry do not matter).
  */
 fp8_status_t fp8_gemm_mx(const uint8_t* qa, int64_t lda, const uint8_t* sa, const uint8_t* qw, int64_t ldw,
                          const uint8_t* sw, uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K, void* ws,

@@ -279,13 +279,13 @@ def test_kv_validation():
 def test_mx_validation():
     L = fp8.lib()
     # x, rows, K, ldx, q, ldq, scales, stream
-    assert L.fp8_quantize_mx(P, 4, 48, 48, Q, 48, P, S0) == FP8_ERR_UNSUPPORTED          # K % 32
-    assert L.fp8_quantize_mx(P, 4, 64, 62, Q, 64, P, S0) == FP8_ERR_INVALID_ARGUMENT     # ldx < K
-    assert L.fp8_quantize_mx(P, 4, 64, 64, Q, 64, 0, S0) == FP8_ERR_INVALID_ARGUMENT     # no scales
-    assert L.fp8_quantize_mx(MIS, 4, 64, 64, Q, 64, P, S0) == FP8_ERR_UNSUPPORTED
-    assert L.fp8_quantize_mx(0, 0, 64, 64, 0, 64, 0, S0) == FP8_OK
+    assert L.fp8_quantize_mx(P, 4, 96, 96, Q, 96, P, S0) == FP8_ERR_UNSUPPORTED          # K % 128
+    assert L.fp8_quantize_mx(P, 4, 128, 126, Q, 128, P, S0) == FP8_ERR_INVALID_ARGUMENT  # ldx < K
+    assert L.fp8_quantize_mx(P, 4, 128, 128, Q, 128, 0, S0) == FP8_ERR_INVALID_ARGUMENT  # no scales
+    assert L.fp8_quantize_mx(MIS, 4, 128, 128, Q, 128, P, S0) == FP8_ERR_UNSUPPORTED
+    assert L.fp8_quantize_mx(0, 0, 128, 128, 0, 128, 0, S0) == FP8_OK
     assert L.fp8_mx_workspace_bytes(64, 8192, 28672) == 4 * 64 * 8192 * 4   # split-K partials
-    assert L.fp8_mx_workspace_bytes(8192, 8192, 8192) == 2 * 8192 * 256      # chunk-major scale copies
+    assert L.fp8_mx_workspace_bytes(8192, 8192, 8192) == 0
     assert L.fp8_mx_workspace_bytes(8, 256, 96) == ctypes.c_size_t(-1).value  # K % 128
     # qa, lda, sa, qw, ldw, sw, y, ldy, M, N, K, ws, ws_bytes, stream
     assert L.fp8_gemm_mx(P, 96, P, Q, 96, P, P, 16, 8, 16, 96, 0, 0, S0) == FP8_ERR_UNSUPPORTED   # K % 128

@@ -15,6 +15,12 @@ from tests._gpu import DEV, assert_codes_equal, assert_within_tolerance, log, to
 pytestmark = pytest.mark.gpu
 
 
+def chunk_major(sc):
+    """Oracle scale bytes [rows, K/32] -> the library's layout [K/128, rows, 4]."""
+    rows, nb = sc.shape
+    return np.ascontiguousarray(sc.reshape(rows, nb // 4, 4).transpose(1, 0, 2))
+
+
 def _rows_with_edges(rows, K, seed):
     x, _ = synth.activations(rows, K, max(1, K // 100), 50.0, seed=seed)
     if rows >= 4 and K >= 128:
@@ -28,7 +34,7 @@ def _rows_with_edges(rows, K, seed):
     return x
 
 
-@pytest.mark.parametrize("rows,K,ld", [(1, 32, 32), (3, 96, 100), (4, 128, 128), (77, 1056, 1056),
+@pytest.mark.parametrize("rows,K,ld", [(1, 128, 128), (3, 256, 260), (4, 128, 128), (77, 1152, 1152),
                                        (600, 4096, 4096), (9, 28672, 28672)])
 def test_quantize_mx_bit_exact(rows, K, ld):
     x = _rows_with_edges(rows, K, seed=rows + K)
@@ -38,7 +44,7 @@ def test_quantize_mx_bit_exact(rows, K, ld):
     q, sc = fp8.fp8_quantize_mx(xd)
     wq, wsc = oracle.quantize_mx(x)
     assert_codes_equal(to_host(q), wq, f"mx codes rows={rows} K={K}")
-    assert_codes_equal(to_host(sc), wsc, f"mx scales rows={rows} K={K}")
+    assert_codes_equal(to_host(sc), chunk_major(wsc), f"mx scales rows={rows} K={K}")
 
 
 GEMM_SHAPES = [(1, 16, 128), (8, 272, 512), (17, 300, 1024), (64, 1000, 4096), (40, 1000, 8320),
@@ -53,7 +59,7 @@ def test_gemm_mx_within_tolerance(M, N, K):
     qa, sa = oracle.quantize_mx(x)
     qw, sw = oracle.quantize_mx(w)
     log(f"  mx gemm M={M} N={N} K={K} ws={fp8.fp8_mx_workspace_bytes(M, N, K)}")
-    y = fp8.fp8_gemm_mx(to_dev(qa), to_dev(sa), to_dev(qw), to_dev(sw))
+    y = fp8.fp8_gemm_mx(to_dev(qa), to_dev(chunk_major(sa)), to_dev(qw), to_dev(chunk_major(sw)))
     if M * N <= 300 * 1040:
         ref, ab = oracle.gemm_mx_ref(qa, sa, qw, sw)
         assert_within_tolerance(to_host(y), ref, ab, f"mx M={M} N={N} K={K}")
@@ -72,7 +78,7 @@ def test_gemm_mx_strided_output_and_stale_workspace():
     qw, sw = oracle.quantize_mx(w)
     ws = torch.full((fp8.fp8_mx_workspace_bytes(M, N, K),), 0x7F, dtype=torch.uint8, device=DEV)
     yb = torch.full((M, N + 24), -7.0, dtype=torch.bfloat16, device=DEV)
-    fp8.fp8_gemm_mx(to_dev(qa), to_dev(sa), to_dev(qw), to_dev(sw), y=yb[:, :N], ws=ws)
+    fp8.fp8_gemm_mx(to_dev(qa), to_dev(chunk_major(sa)), to_dev(qw), to_dev(chunk_major(sw)), y=yb[:, :N], ws=ws)
     got = to_host(yb)
     rng = np.random.default_rng(3)
     ms, ns = rng.integers(0, M, 20000), rng.integers(0, N, 20000)
@@ -95,9 +101,9 @@ def test_mx_end_to_end_full_size(name):
     y = fp8.fp8_gemm_mx(qa, sa, qw, sw)
     oqa, osa = oracle.quantize_mx(x)
     assert_codes_equal(to_host(qa), oqa, "activation codes")
-    assert_codes_equal(to_host(sa), osa, "activation scales")
+    assert_codes_equal(to_host(sa), chunk_major(osa), "activation scales")
     oqw, osw = oracle.quantize_mx(wt)
-    assert_codes_equal(to_host(sw), osw, "weight scales")
+    assert_codes_equal(to_host(sw), chunk_major(osw), "weight scales")
     qw_h = to_host(qw)
     assert_codes_equal(qw_h, oqw, "weight codes")
     rng = np.random.default_rng(1)
@@ -118,6 +124,6 @@ def test_gemm_mx_random_codes_and_scales(M, N, K):
     qw[(qw & 0x7F) == 0x7F] = 0x41
     sa = rng.integers(119, 136, (M, K // 32), dtype=np.uint8)
     sw = rng.integers(119, 136, (N, K // 32), dtype=np.uint8)
-    y = fp8.fp8_gemm_mx(to_dev(qa), to_dev(sa), to_dev(qw), to_dev(sw))
+    y = fp8.fp8_gemm_mx(to_dev(qa), to_dev(chunk_major(sa)), to_dev(qw), to_dev(chunk_major(sw)))
     ref, ab = oracle.gemm_mx_ref(qa, sa, qw, sw)
     assert_within_tolerance(to_host(y), ref, ab, f"mx random M={M} N={N} K={K}")
