@@ -508,7 +508,9 @@ def bench_mx(args, w, dev, steps, warmup, graph, log):
         roof = dict(bound="mfma", achieved=round(ach, 1), peak=FP8_PEAK_TFLOPS, unit="TFLOP/s",
                     frac=round(ach / FP8_PEAK_TFLOPS, 4), per_launch=f"{flops:.6g} FLOP")
         kernel = "gemm_mfma_kernel (block-scaled)"
-    roof.update(kernel=kernel, avg_launch_us=round(g_ms * 1e3, 3), traffic=None)
+    roof.update(kernel=kernel, avg_launch_us=round(g_ms * 1e3, 3),
+                traffic=read_traffic(f"{args.workload}@mx", "skinny" if decode else "mfma",
+                                     "gemm_skinny_kernel" if decode else "gemm_mfma_kernel"))
     cfg = dict(workload=args.workload, M=M, N=N, K=K, seed=args.seed, weight_copies=copies,
                step="fp8_quantize_mx + fp8_gemm_mx", scales="32-element blocks, power-of-two (E8M0)", out="bf16")
     extra = dict(timing="hip-graph replay of the steps" if graph else "eager launches", step_us=round(ms * 1e3, 3),
