@@ -55,7 +55,17 @@ __global__ __launch_bounds__(KW * 64) void gemm_skinny_kernel(
     const int n0 = blockIdx.x * (NT * 16);
     const int c0 = blockIdx.z * split_chunks;
     const int nchunks = min((K + 127) >> 7, c0 + split_chunks) - c0;
-    const int steps = nchunks > wave ? (nchunks - wave + KW - 1) / KW : 0;
+    // Chunk order of a wave: interleaved (wave w: chunks w, w + KW, ...) for
+    // one activation tile, whose one-kernel fused variant must add in the same
+    // order; with more tiles (M > 16), one contiguous range per wave, which
+    // streams a 235 MB weight matrix markedly faster (measured on MI355X with
+    // the same loads and no arithmetic: 44 vs 52 us for 128-row workgroups).
+    constexpr bool CONTIG = MT > 1;
+    const int per = (nchunks + KW - 1) / KW;
+    const int cw0 = CONTIG ? c0 + wave * per : c0 + wave;
+    const int steps = CONTIG ? max(0, min(nchunks - wave * per, per))
+                             : (nchunks > wave ? (nchunks - wave + KW - 1) / KW : 0);
+    auto chunk_of = [&](int s) { return CONTIG ? cw0 + s : cw0 + KW * s; };
 
     const uint8_t* wrow[NT];
 #pragma unroll
@@ -105,7 +115,7 @@ __global__ __launch_bounds__(KW * 64) void gemm_skinny_kernel(
     // K read the row's first bytes (K >= 16 whenever a step runs).  Rows past
     // N or M read row 0: they only feed output elements that are never stored.
     auto load_step = [&](int s, int d) {
-        const int kb = (c0 + wave + KW * s) * 128;
+        const int kb = chunk_of(s) * 128;
         const int o0 = kb + 16 * g < K ? kb + 16 * g : 0;
         const int o1 = kb + 64 + 16 * g < K ? kb + 64 + 16 * g : 0;
 #pragma unroll
@@ -139,7 +149,7 @@ __global__ __launch_bounds__(KW * 64) void gemm_skinny_kernel(
 #pragma unroll
             for (int d = 0; d < DEPTH; ++d) {
                 const int s = s0 + d;
-                const int kb = (c0 + wave + KW * s) * 128;
+                const int kb = chunk_of(s) * 128;
                 const bool ok0 = s < steps && kb + 16 * g < K;
                 const bool ok1 = s < steps && kb + 64 + 16 * g < K;
                 v8i xf[MT];
