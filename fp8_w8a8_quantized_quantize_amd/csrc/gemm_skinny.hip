@@ -478,6 +478,9 @@ static void launch_mt(int nt, dim3 grid, hipStream_t stream, const uint8_t* qa, 
                       int N, int K, float* part, int split_chunks, MxScales mx) {
     switch (nt) {
         case 8: launch_cfg<MT, 8, 4, MX>(grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, y32, ldy, M, N, K, part, split_chunks, mx); break;
+        case 7: launch_cfg<MT, 7, 4, MX>(grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, y32, ldy, M, N, K, part, split_chunks, mx); break;
+        case 6: launch_cfg<MT, 6, 4, MX>(grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, y32, ldy, M, N, K, part, split_chunks, mx); break;
+        case 5: launch_cfg<MT, 5, 4, MX>(grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, y32, ldy, M, N, K, part, split_chunks, mx); break;
         case 4: launch_cfg<MT, 4, 8, MX>(grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, y32, ldy, M, N, K, part, split_chunks, mx); break;
         case 2: launch_cfg<MT, 2, 8, MX>(grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, y32, ldy, M, N, K, part, split_chunks, mx); break;
         default: launch_cfg<MT, 1, 8, MX>(grid, stream, qa, lda, s_tok, qw, ldw, s_ch, y, y32, ldy, M, N, K, part, split_chunks, mx); break;
@@ -490,12 +493,14 @@ static void launch_mt(int nt, dim3 grid, hipStream_t stream, const uint8_t* qa, 
 // workgroup per CU (measured on MI355X: 256 workgroups of 4 waves, one per
 // CU, beat partial second rounds).  One activation tile (M <= 16): the largest
 // nt <= 4 that leaves >= 224 workgroups, never split (the one-kernel fused
-// path must produce the same bits).  More tiles: nt = 8 (4 waves) when that
-// leaves >= 224 workgroups; when it leaves at most 128, k is split into
-// floor(256 / workgroups) parts (each keeping at least two 128-byte chunks
-// per wave); in between, nt = 4 (8 waves).  Split workgroups write fp32
-// partial sums to the workspace, which a second kernel adds up in a fixed
-// order.
+// path must produce the same bits).  More tiles: when nt = 8 (4 waves)
+// leaves >= 224 workgroups, the smallest nt in 5..8 that still leaves at most
+// 256 (the 70B gate/up shape: nt = 7 gives exactly 256 workgroups and
+// measured 50.7 us against 55.7 us for nt = 8's 224); when it leaves at most
+// 128, k is split into floor(256 / workgroups) parts (each keeping at least
+// two 128-byte chunks per wave); in between, nt = 4 (8 waves).  Split
+// workgroups write fp32 partial sums to the workspace, which a second kernel
+// adds up in a fixed order.
 SkinnyPlan skinny_plan(int64_t M, int64_t N, int64_t K) {
     SkinnyPlan p{};
     p.mt = (int)((M + 15) / 16);
@@ -515,6 +520,7 @@ SkinnyPlan skinny_plan(int64_t M, int64_t N, int64_t K) {
     const int64_t g8 = groups(8);
     if (g8 >= 224) {
         p.nt = 8;
+        for (int c = 7; c >= 5 && groups(c) <= 256; --c) p.nt = c;
         return p;
     }
     if (g8 > 128) {
@@ -548,8 +554,11 @@ static hipError_t launch_skinny_any(const uint8_t* qa, int64_t lda, const float*
     if (M <= 0 || N <= 0) return hipSuccess;
     SkinnyPlan p = skinny_plan(M, N, K);
     // MX: 4 activation tiles with nt = 4 (8 waves, 256 VGPRs each) would
-    // spill; take nt = 8 (4 waves) there (same splits: none on this branch)
+    // spill; take nt = 8 (4 waves) there (same splits: none on this branch).
+    // The shallower MX prefetch also measured slower with nt = 5..7 than
+    // with nt = 8 (70B gate/up: 62.8 vs 60.8 us), so MX keeps nt = 8.
     if (MX && p.mt == 4 && p.nt == 4) p.nt = 8;
+    if (MX && p.nt >= 5 && p.nt <= 7) p.nt = 8;
     float* part = p.splits > 1 ? static_cast<float*>(ws) : nullptr;
     const dim3 grid((unsigned)((N + 16 * p.nt - 1) / (16 * p.nt)), 1, (unsigned)p.splits);
     const int m = (int)M, n = (int)N, k = (int)K;
