@@ -293,3 +293,34 @@ def test_mx_validation():
     assert L.fp8_gemm_mx(P, 128, 0, Q, 128, P, P, 16, 8, 16, 128, 0, 0, S0) == FP8_ERR_INVALID_ARGUMENT
     assert L.fp8_gemm_mx(P, 28672, P, Q, 28672, P, P, 8192, 64, 8192, 28672, 0, 0, S0) == FP8_ERR_WORKSPACE
     assert L.fp8_gemm_mx(P, 128, P, Q, 128, P, P, 16, 0, 16, 128, 0, 0, S0) == FP8_OK
+
+
+@pytest.mark.parametrize("call", ["quantize_static", "quantize_clipped", "calibrate", "fp8out", "quantize_mx",
+                                  "gemm_mx", "kv_scales", "kv_quantize", "kv_dequantize", "kv_format"])
+def test_python_bindings_reject_host_tensors_and_bad_arguments(call):
+    """The bindings only marshal arguments: host tensors, wrong dtypes or shapes
+    and unknown formats raise before anything reaches the library."""
+    import torch
+    x = torch.zeros(4, 128)
+    u8 = torch.zeros(4, 128, dtype=torch.uint8)
+    with pytest.raises((TypeError, ValueError)):
+        if call == "quantize_static":
+            fp8.fp8_quantize_static(x, torch.ones(1))
+        elif call == "quantize_clipped":
+            fp8.fp8_quantize_per_token_clipped(x, torch.ones(1))
+        elif call == "calibrate":
+            fp8.fp8_calibrate_percentile(x, 999, 1000)
+        elif call == "fp8out":
+            fp8.fp8_gemm_scaled_fp8out(u8, torch.ones(4), u8, torch.ones(4))
+        elif call == "quantize_mx":
+            fp8.fp8_quantize_mx(x)
+        elif call == "gemm_mx":
+            fp8.fp8_gemm_mx(u8, torch.zeros(1, 4, 4, dtype=torch.uint8), u8, torch.zeros(1, 4, 4, dtype=torch.uint8))
+        elif call == "kv_scales":
+            fp8.fp8_kv_channel_scales(x, "e5m2")
+        elif call == "kv_quantize":
+            fp8.fp8_kv_quantize_paged(x, torch.ones(128), torch.zeros(4, dtype=torch.int32), u8, "e5m2")
+        elif call == "kv_dequantize":
+            fp8.fp8_kv_dequantize_paged(u8, torch.zeros(4, dtype=torch.int32), torch.ones(128), "e5m2")
+        else:
+            fp8._kv_fmt("e4m2")
