@@ -52,8 +52,7 @@ def lib():
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is not built: run __graft_entry__.build() "
-                               "(or python fp8_w8a8_quantized_quantize_amd/_build.py)")
+            raise RuntimeError(f"{LIB_PATH} is not built: run python fp8_w8a8_quantized_quantize_amd/_build.py")
         L = ctypes.CDLL(LIB_PATH)
         i64, vp, sz, st = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
         L.fp8_quantize_per_token.restype = st

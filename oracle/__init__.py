@@ -34,7 +34,7 @@ def lib():
     global _lib
     if _lib is None:
         if not os.path.exists(_LIB_PATH):
-            raise RuntimeError(f"{_LIB_PATH} is missing: run `python oracle/build.py` (or __graft_entry__.build())")
+            raise RuntimeError(f"{_LIB_PATH} is missing: run `python oracle/build.py`")
         L = ctypes.CDLL(_LIB_PATH)
         i64, vp, f64 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_double
         L.oracle_e4m3_decode.restype = f64

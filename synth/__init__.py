@@ -29,7 +29,7 @@ def lib():
     global _lib
     if _lib is None:
         if not os.path.exists(_LIB_PATH):
-            raise RuntimeError(f"{_LIB_PATH} is missing: run `python synth/build.py` (or __graft_entry__.build())")
+            raise RuntimeError(f"{_LIB_PATH} is missing: run `python synth/build.py`")
         L = ctypes.CDLL(_LIB_PATH)
         u64, i64, f32, f64 = ctypes.c_uint64, ctypes.c_int64, ctypes.c_float, ctypes.c_double
         vp = ctypes.c_void_p
