@@ -66,6 +66,8 @@ def parse():
     ap.add_argument("--scales", choices=("token", "mx"), default="token",
                     help="token: per-token x per-channel scales (default); mx: 32-element block scales "
                          "(fp8_quantize_mx + fp8_gemm_mx, dense workloads)")
+    ap.add_argument("--kv-dtype", choices=("bf16", "f16", "f32"), default=None,
+                    help="element type of the KV rows and of the read back (KV workloads; default: the workload's)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run 5 plain device copies of 512 MiB (reference for rocprofv3 FETCH/WRITE_SIZE)")
     ap.add_argument("--profile", action="store_true",
@@ -539,18 +541,21 @@ def bench_kv(args, w, dev, steps, warmup, graph, log):
     import fp8_w8a8_quantized_quantize_amd as fp8
     import synth
     T, C, B, fmt = w["T"], w["C"], w["block"], w["fmt"]
+    kvdt = args.kv_dtype or w["dtype"]
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[kvdt]
+    eb = 4 if kvdt == "f32" else 2
     nb = T // B + 256
-    log(f"[bench] {args.workload}: generating inputs T={T} C={C} block={B} blocks={nb} fmt={fmt}")
+    log(f"[bench] {args.workload}: generating inputs T={T} C={C} block={B} blocks={nb} fmt={fmt} rows={kvdt}")
     kv = synth.kv_activations(T, C, seed=args.seed)
     slot = synth.kv_slot_mapping(T, B, nb, seed=args.seed)
-    copies = 2
-    kvd = [torch.from_numpy(kv).to(dev)]
+    copies = 2 if eb == 4 else 3   # >= 400 MB of rows rotated past the Infinity Cache
+    kvd = [torch.from_numpy(kv).to(dev).to(tdt)]
     kvd += [kvd[0].clone() for _ in range(copies - 1)]
     slotd = torch.from_numpy(slot).to(dev)
     cache = torch.zeros((nb * B, C), dtype=torch.uint8, device=dev)
     scales = torch.empty(C, dtype=torch.float32, device=dev)
     ws = torch.empty(fp8.fp8_kv_scales_workspace_bytes(T, C), dtype=torch.uint8, device=dev)
-    out = torch.empty((T, C), dtype=torch.float32, device=dev)
+    out = torch.empty((T, C), dtype=tdt, device=dev)
 
     def step(i):
         fp8.fp8_kv_channel_scales(kvd[i % copies], fmt, scales=scales, ws=ws)
@@ -572,16 +577,16 @@ def bench_kv(args, w, dev, steps, warmup, graph, log):
     dq_ms, _ = time_loop(read_back, steps, warmup, graph)
     ms, sc_ms, q_ms, dq_ms = total_ms / steps, sc_ms / steps, q_ms / steps, dq_ms / steps
     # algorithmic bytes: the batch read once, codes written once, scales and slots
-    step_bytes = 4 * T * C + T * C + 4 * C + 4 * T
-    scale_bytes = 4 * T * C + 4 * C
-    quant_bytes = 4 * T * C + 4 * C + 4 * T + T * C
-    dq_bytes = T * C + 4 * T + 4 * C + 4 * T * C
+    step_bytes = eb * T * C + T * C + 4 * C + 4 * T
+    scale_bytes = eb * T * C + 4 * C
+    quant_bytes = eb * T * C + 4 * C + 4 * T + T * C
+    dq_bytes = T * C + 4 * T + 4 * C + eb * T * C
     gbs = lambda b, t: b / (t * 1e-3) / 1e9
     value = gbs(step_bytes, ms)
     q_ach = gbs(quant_bytes, q_ms)
     roof = dict(bound="hbm", achieved=round(q_ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                 frac=round(q_ach / HBM_PEAK_GBS, 4), kernel="kv_quantize_paged",
-                per_launch=f"{quant_bytes} algorithmic bytes (fp32 kv in, slots, scales, FP8 codes out)",
+                per_launch=f"{quant_bytes} algorithmic bytes ({kvdt} kv in, slots, scales, FP8 codes out)",
                 avg_launch_us=round(q_ms * 1e3, 3), traffic=read_traffic(args.workload, "kv", "kv_quantize_paged"),
                 others=dict(channel_scales=dict(kernels="kv_amax_partial + kv_scale_finish",
                                                 avg_us=round(sc_ms * 1e3, 3), achieved=round(gbs(scale_bytes, sc_ms), 1),
@@ -591,10 +596,11 @@ def bench_kv(args, w, dev, steps, warmup, graph, log):
                                            achieved=round(gbs(dq_bytes, dq_ms), 1),
                                            frac=round(gbs(dq_bytes, dq_ms) / HBM_PEAK_GBS, 4),
                                            per_launch=f"{dq_bytes} algorithmic bytes")))
-    cfg = dict(workload=args.workload, T=T, C=C, block=B, blocks=nb, fmt=fmt, seed=args.seed, kv_copies=copies,
+    cfg = dict(workload=args.workload, T=T, C=C, block=B, blocks=nb, fmt=fmt, rows=kvdt, seed=args.seed,
+               kv_copies=copies,
                step="fp8_kv_channel_scales + fp8_kv_quantize_paged")
     extra = dict(timing="hip-graph replay of the steps" if graph else "eager launches", step_us=round(ms * 1e3, 3),
-                 step_gbs_counting_both_reads=round(gbs(step_bytes + 4 * T * C, ms), 1))
+                 step_gbs_counting_both_reads=round(gbs(step_bytes + eb * T * C, ms), 1))
     if per:
         extra.update(step_us_median=round(pct(per, 0.5) * 1e3, 3))
     cpu = None
@@ -603,6 +609,7 @@ def bench_kv(args, w, dev, steps, warmup, graph, log):
         log("[bench] timing the CPU oracle")
         rows = min(T, 4096)
         fid = oracle.E5M2 if fmt == "e5m2" else oracle.E4M3
+        kv = kvd[0][:rows].float().cpu().numpy()   # the values the rows hold
         # the sample's slots, renumbered into a cache of `rows` rows (same scatter order)
         compact = np.empty(rows, dtype=np.int32)
         compact[np.argsort(slot[:rows], kind="stable")] = np.arange(rows, dtype=np.int32)
@@ -615,7 +622,7 @@ def bench_kv(args, w, dev, steps, warmup, graph, log):
             elapsed = time.perf_counter() - t0
             if elapsed >= args.cpu_seconds:
                 break
-        b = reps * (4 * rows * C + rows * C + 4 * C + 4 * rows)
+        b = reps * (eb * rows * C + rows * C + 4 * C + 4 * rows)
         cpu = dict(value=round(b / elapsed / 1e9, 6), unit="GB/s", cores=oracle.num_threads(), kind="oracle",
                    seconds=round(elapsed, 2),
                    sample=f"{reps} pass(es) of channel scales + paged quantize over the first {rows} of {T} tokens "
@@ -623,7 +630,7 @@ def bench_kv(args, w, dev, steps, warmup, graph, log):
     res = {
         "metric": METRIC, "value": round(value, 3), "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": f"fp32 in, {fmt} codes", "data": "synthetic (seeded; no dataset, no trained weights)",
+        "dtype": f"{kvdt} in, {fmt} codes", "data": "synthetic (seeded; no dataset, no trained weights)",
         "config": cfg, "roofline": roof, "cpu_baseline": cpu, "detail": extra,
     }
     print(json.dumps(res), flush=True)

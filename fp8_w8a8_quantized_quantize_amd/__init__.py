@@ -86,13 +86,13 @@ def lib():
         L.fp8_mx_workspace_bytes.restype = sz
         L.fp8_mx_workspace_bytes.argtypes = [i64, i64, i64]
         L.fp8_kv_channel_scales.restype = st
-        L.fp8_kv_channel_scales.argtypes = [vp, i64, i64, i64, st, vp, vp, sz, vp]
+        L.fp8_kv_channel_scales.argtypes = [vp, st, i64, i64, i64, st, vp, vp, sz, vp]
         L.fp8_kv_scales_workspace_bytes.restype = sz
         L.fp8_kv_scales_workspace_bytes.argtypes = [i64, i64]
         L.fp8_kv_quantize_paged.restype = st
-        L.fp8_kv_quantize_paged.argtypes = [vp, i64, i64, i64, vp, st, vp, vp, i64, vp]
+        L.fp8_kv_quantize_paged.argtypes = [vp, st, i64, i64, i64, vp, st, vp, vp, i64, vp]
         L.fp8_kv_dequantize_paged.restype = st
-        L.fp8_kv_dequantize_paged.argtypes = [vp, i64, vp, i64, i64, vp, st, vp, i64, vp]
+        L.fp8_kv_dequantize_paged.argtypes = [vp, i64, vp, i64, i64, vp, st, vp, st, i64, vp]
         L.fp8_status_string.restype = ctypes.c_char_p
         L.fp8_status_string.argtypes = [st]
         _lib = L
@@ -277,6 +277,9 @@ def fp8_gemm_mx(qa, sa, qw, sw, y=None, ws=None, stream=None):
 
 FP8_KV_E4M3 = 0
 FP8_KV_E5M2 = 1
+FP8_KV_F32 = 0
+FP8_KV_BF16 = 1
+FP8_KV_F16 = 2
 _KV_FORMATS = {"e4m3": FP8_KV_E4M3, "e5m2": FP8_KV_E5M2, FP8_KV_E4M3: FP8_KV_E4M3, FP8_KV_E5M2: FP8_KV_E5M2}
 
 
@@ -290,11 +293,26 @@ def fp8_kv_scales_workspace_bytes(T, C):
     return int(lib().fp8_kv_scales_workspace_bytes(T, C))
 
 
-def fp8_kv_channel_scales(kv, fmt="e5m2", scales=None, ws=None, stream=None):
-    """Per-channel scales max(fl32(max_t |kv[t,c]| / fmt_max), 1e-12f) of fp32
-    kv [T, C] -> scales fp32 [C]."""
+def _kv_dtype(t, name):
     torch = _torch()
-    T, C, ldkv = _rows(kv, torch.float32, "kv")
+    codes = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
+    if not isinstance(t, torch.Tensor) or t.dtype not in codes or not t.is_cuda:
+        raise TypeError(f"{name}: expected a float32, bfloat16 or float16 CUDA tensor")
+    return codes[t.dtype]
+
+
+def _kv_rows(t, name):
+    dt = _kv_dtype(t, name)
+    if t.dim() != 2 or (t.shape[0] > 0 and t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError(f"{name}: expected a 2-D row-major tensor (unit stride along the last dim)")
+    return t.shape[0], t.shape[1], (t.stride(0) if t.shape[0] > 1 else t.shape[1]), dt
+
+
+def fp8_kv_channel_scales(kv, fmt="e5m2", scales=None, ws=None, stream=None):
+    """Per-channel scales max(fl32(max_t |kv[t,c]| / fmt_max), 1e-12f) of kv [T, C]
+    (float32, bfloat16 or float16) -> scales fp32 [C]."""
+    torch = _torch()
+    T, C, ldkv, dt = _kv_rows(kv, "kv")
     if scales is None:
         scales = torch.empty(C, dtype=torch.float32, device=kv.device)
     _vec(scales, torch.float32, "scales", C)
@@ -304,29 +322,31 @@ def fp8_kv_channel_scales(kv, fmt="e5m2", scales=None, ws=None, stream=None):
             raise Fp8Error("fp8_kv_channel_scales", 2)
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=kv.device)
     _check("fp8_kv_channel_scales",
-           lib().fp8_kv_channel_scales(_ptr(kv), T, C, ldkv, _kv_fmt(fmt), _ptr(scales), _ptr(ws),
+           lib().fp8_kv_channel_scales(_ptr(kv), dt, T, C, ldkv, _kv_fmt(fmt), _ptr(scales), _ptr(ws),
                                        ws.numel() * ws.element_size(), _stream(stream)))
     return scales
 
 
 def fp8_kv_quantize_paged(kv, scales, slot_mapping, cache, fmt="e5m2", stream=None):
-    """Write fp32 kv [T, C] into the rows slot_mapping[t] of the uint8 cache
-    [num_slots, C] (contiguous) as FP8 codes of kv / scales; returns cache."""
+    """Write kv [T, C] (float32, bfloat16 or float16) into the rows slot_mapping[t]
+    of the uint8 cache [num_slots, C] (contiguous) as FP8 codes of kv / scales;
+    returns cache."""
     torch = _torch()
-    T, C, ldkv = _rows(kv, torch.float32, "kv")
+    T, C, ldkv, dt = _kv_rows(kv, "kv")
     _vec(scales, torch.float32, "scales", C)
     _vec(slot_mapping, torch.int32, "slot_mapping", T)
     if not isinstance(cache, torch.Tensor) or cache.dtype != torch.uint8 or not cache.is_cuda \
             or not cache.is_contiguous() or cache.dim() != 2 or cache.shape[1] != C:
         raise TypeError("cache: expected a contiguous uint8 CUDA tensor [num_slots, C]")
     _check("fp8_kv_quantize_paged",
-           lib().fp8_kv_quantize_paged(_ptr(kv), T, C, ldkv, _ptr(scales), _kv_fmt(fmt), _ptr(slot_mapping),
+           lib().fp8_kv_quantize_paged(_ptr(kv), dt, T, C, ldkv, _ptr(scales), _kv_fmt(fmt), _ptr(slot_mapping),
                                        _ptr(cache), cache.shape[0], _stream(stream)))
     return cache
 
 
-def fp8_kv_dequantize_paged(cache, slot_mapping, scales, fmt="e5m2", out=None, stream=None):
-    """Read cache rows slot_mapping[t] back -> fp32 out [T, C]."""
+def fp8_kv_dequantize_paged(cache, slot_mapping, scales, fmt="e5m2", out=None, out_dtype=None, stream=None):
+    """Read cache rows slot_mapping[t] back -> out [T, C] (float32 by default, or
+    bfloat16 / float16: out's dtype, else out_dtype)."""
     torch = _torch()
     if not isinstance(cache, torch.Tensor) or cache.dtype != torch.uint8 or not cache.is_cuda \
             or not cache.is_contiguous() or cache.dim() != 2:
@@ -336,13 +356,13 @@ def fp8_kv_dequantize_paged(cache, slot_mapping, scales, fmt="e5m2", out=None, s
     _vec(slot_mapping, torch.int32, "slot_mapping", T)
     _vec(scales, torch.float32, "scales", C)
     if out is None:
-        out = torch.empty((T, C), dtype=torch.float32, device=cache.device)
-    T2, C2, ldo = _rows(out, torch.float32, "out")
+        out = torch.empty((T, C), dtype=out_dtype or torch.float32, device=cache.device)
+    T2, C2, ldo, odt = _kv_rows(out, "out")
     if (T2, C2) != (T, C):
         raise ValueError("out: expected shape [T, C]")
     _check("fp8_kv_dequantize_paged",
            lib().fp8_kv_dequantize_paged(_ptr(cache), num_slots, _ptr(slot_mapping), T, C, _ptr(scales),
-                                         _kv_fmt(fmt), _ptr(out), ldo, _stream(stream)))
+                                         _kv_fmt(fmt), _ptr(out), odt, ldo, _stream(stream)))
     return out
 
 

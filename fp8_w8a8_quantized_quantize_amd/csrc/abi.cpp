@@ -72,6 +72,7 @@ fp8_status_t check_vector(const void* p, int64_t n) {
     } while (0)
 
 static_assert(FP8_KV_E4M3 == fp8k::kKvE4M3 && FP8_KV_E5M2 == fp8k::kKvE5M2, "KV format ids");
+static_assert(FP8_KV_F32 == fp8k::kKvF32 && FP8_KV_BF16 == fp8k::kKvBF16 && FP8_KV_F16 == fp8k::kKvF16, "KV dtype ids");
 
 // KV batch extents: C channels in groups of 4 (one 32-bit word of codes).
 fp8_status_t check_kv_dims(int64_t T, int64_t C) {
@@ -83,6 +84,25 @@ fp8_status_t check_kv_dims(int64_t T, int64_t C) {
 
 fp8_status_t check_kv_format(fp8_kv_format_t fmt) {
     return (fmt == FP8_KV_E4M3 || fmt == FP8_KV_E5M2) ? FP8_OK : FP8_ERR_INVALID_ARGUMENT;
+}
+
+// Element size of a KV row type, 0 when the type is unknown.
+int64_t kv_elem_bytes(fp8_kv_dtype_t t) {
+    switch (t) {
+        case FP8_KV_F32: return 4;
+        case FP8_KV_BF16:
+        case FP8_KV_F16: return 2;
+    }
+    return 0;
+}
+
+// Element size of a KV row type and the channel rule that goes with it:
+// 16-bit rows are read 8 channels (16 bytes) per thread, so C % 8 == 0.
+fp8_status_t kv_row_type(fp8_kv_dtype_t t, int64_t C, int64_t* eb) {
+    *eb = kv_elem_bytes(t);
+    if (*eb == 0) return FP8_ERR_INVALID_ARGUMENT;
+    if (*eb == 2 && C % 8 != 0) return FP8_ERR_UNSUPPORTED;
+    return FP8_OK;
 }
 
 fp8_status_t from_hip(hipError_t e) { return e == hipSuccess ? FP8_OK : FP8_ERR_DEVICE; }
@@ -249,52 +269,59 @@ size_t fp8_kv_scales_workspace_bytes(int64_t T, int64_t C) {
     return round_up(fp8k::kv_scales_ws_bytes(T, C), kAlign);
 }
 
-fp8_status_t fp8_kv_channel_scales(const float* kv, int64_t T, int64_t C, int64_t ldkv, fp8_kv_format_t fmt,
-                                   float* scales, void* ws, size_t ws_bytes, hipStream_t stream) {
+fp8_status_t fp8_kv_channel_scales(const void* kv, fp8_kv_dtype_t kv_dtype, int64_t T, int64_t C, int64_t ldkv,
+                                   fp8_kv_format_t fmt, float* scales, void* ws, size_t ws_bytes,
+                                   hipStream_t stream) {
     FP8_TRY(check_kv_dims(T, C));
     FP8_TRY(check_kv_format(fmt));
-    FP8_TRY(check_matrix(kv, T, C, ldkv, 4));
+    int64_t eb = 0;
+    FP8_TRY(kv_row_type(kv_dtype, C, &eb));
+    FP8_TRY(check_matrix(kv, T, C, ldkv, eb));
     FP8_TRY(check_vector(scales, C));
     if (C == 0) return FP8_OK;
     const size_t need = round_up(fp8k::kv_scales_ws_bytes(T, C), kAlign);
     if (ws_bytes < need) return FP8_ERR_WORKSPACE;
     if (ws == nullptr) return FP8_ERR_INVALID_ARGUMENT;
     if (!aligned16(ws)) return FP8_ERR_UNSUPPORTED;
-    return from_hip(fp8k::launch_kv_channel_scales(kv, T, C, ldkv, (int)fmt, scales, ws, stream));
+    return from_hip(fp8k::launch_kv_channel_scales(kv, (int)kv_dtype, T, C, ldkv, (int)fmt, scales, ws, stream));
 }
 
-fp8_status_t fp8_kv_quantize_paged(const float* kv, int64_t T, int64_t C, int64_t ldkv, const float* scales,
-                                   fp8_kv_format_t fmt, const int32_t* slot_mapping, uint8_t* cache,
-                                   int64_t num_slots, hipStream_t stream) {
+fp8_status_t fp8_kv_quantize_paged(const void* kv, fp8_kv_dtype_t kv_dtype, int64_t T, int64_t C, int64_t ldkv,
+                                   const float* scales, fp8_kv_format_t fmt, const int32_t* slot_mapping,
+                                   uint8_t* cache, int64_t num_slots, hipStream_t stream) {
     FP8_TRY(check_kv_dims(T, C));
     FP8_TRY(check_kv_format(fmt));
+    int64_t eb = 0;
+    FP8_TRY(kv_row_type(kv_dtype, C, &eb));
     if (num_slots < 0) return FP8_ERR_INVALID_ARGUMENT;
     if (num_slots > kMaxDim) return FP8_ERR_UNSUPPORTED;
-    FP8_TRY(check_matrix(kv, T, C, ldkv, 4));
+    FP8_TRY(check_matrix(kv, T, C, ldkv, eb));
     FP8_TRY(check_vector(scales, T > 0 ? C : 0));
     FP8_TRY(check_matrix(cache, num_slots, C, C, 1, true));
     if (T > 0 && slot_mapping == nullptr) return FP8_ERR_INVALID_ARGUMENT;
     if (T > 0 && (reinterpret_cast<uintptr_t>(slot_mapping) & 3u) != 0) return FP8_ERR_UNSUPPORTED;
     if (T == 0 || C == 0 || num_slots == 0) return FP8_OK;
-    return from_hip(fp8k::launch_kv_quantize_paged(kv, T, C, ldkv, scales, (int)fmt, slot_mapping, cache, num_slots,
-                                                   stream));
+    return from_hip(fp8k::launch_kv_quantize_paged(kv, (int)kv_dtype, T, C, ldkv, scales, (int)fmt, slot_mapping,
+                                                   cache, num_slots, stream));
 }
 
 fp8_status_t fp8_kv_dequantize_paged(const uint8_t* cache, int64_t num_slots, const int32_t* slot_mapping,
-                                     int64_t T, int64_t C, const float* scales, fp8_kv_format_t fmt, float* out,
-                                     int64_t ldo, hipStream_t stream) {
+                                     int64_t T, int64_t C, const float* scales, fp8_kv_format_t fmt, void* out,
+                                     fp8_kv_dtype_t out_dtype, int64_t ldo, hipStream_t stream) {
     FP8_TRY(check_kv_dims(T, C));
     FP8_TRY(check_kv_format(fmt));
+    int64_t eb = 0;
+    FP8_TRY(kv_row_type(out_dtype, C, &eb));
     if (num_slots < 0) return FP8_ERR_INVALID_ARGUMENT;
     if (num_slots > kMaxDim) return FP8_ERR_UNSUPPORTED;
     FP8_TRY(check_matrix(cache, num_slots, C, C, 1, true));
-    FP8_TRY(check_matrix(out, T, C, ldo, 4));
+    FP8_TRY(check_matrix(out, T, C, ldo, eb));
     FP8_TRY(check_vector(scales, T > 0 ? C : 0));
     if (T > 0 && slot_mapping == nullptr) return FP8_ERR_INVALID_ARGUMENT;
     if (T > 0 && (reinterpret_cast<uintptr_t>(slot_mapping) & 3u) != 0) return FP8_ERR_UNSUPPORTED;
     if (T == 0 || C == 0) return FP8_OK;
-    return from_hip(fp8k::launch_kv_dequantize_paged(cache, num_slots, slot_mapping, T, C, scales, (int)fmt, out, ldo,
-                                                     stream));
+    return from_hip(fp8k::launch_kv_dequantize_paged(cache, num_slots, slot_mapping, T, C, scales, (int)fmt, out,
+                                                     (int)out_dtype, ldo, stream));
 }
 
 fp8_status_t fp8_gemm_scaled(const uint8_t* qa, int64_t lda, const float* s_tok, const uint8_t* qw,

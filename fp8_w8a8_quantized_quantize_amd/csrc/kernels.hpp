@@ -25,23 +25,29 @@ constexpr size_t kCalibrateWsBytes = 2048;
 hipError_t launch_calibrate_percentile(const float* x, int64_t n, int64_t rank, float* value_out, float* scale_out,
                                        void* ws, hipStream_t stream);
 
-// FP8 KV-cache codec (kv_cache.hip).  fmt: kKvE4M3 or kKvE5M2.  C % 4 == 0,
-// kv / out row strides multiples of 4 elements, scales 16-byte aligned.
+// FP8 KV-cache codec (kv_cache.hip).  fmt: kKvE4M3 or kKvE5M2; element
+// types of the KV rows and of the read back: kKvF32, kKvBF16, kKvF16.
+// C % 4 == 0, row strides in elements with 16-byte aligned rows, scales
+// 16-byte aligned.
 constexpr int kKvE4M3 = 0;
 constexpr int kKvE5M2 = 1;
+constexpr int kKvF32 = 0;
+constexpr int kKvBF16 = 1;
+constexpr int kKvF16 = 2;
 // Row chunks of the per-channel maximum pass; its fp32 partials take
 // kv_scales_ws_bytes(T, C) bytes of workspace (16-byte aligned).
 struct KvChunks {
     int rows_per_chunk, chunks;
 };
-KvChunks kv_amax_chunks(int64_t T, int64_t C);
+KvChunks kv_amax_chunks(int64_t T, int64_t C, int quads);
 size_t kv_scales_ws_bytes(int64_t T, int64_t C);
-hipError_t launch_kv_channel_scales(const float* kv, int64_t T, int64_t C, int64_t ldkv, int fmt, float* scales,
-                                    void* ws, hipStream_t stream);
-hipError_t launch_kv_quantize_paged(const float* kv, int64_t T, int64_t C, int64_t ldkv, const float* scales, int fmt,
-                                    const int32_t* slot, uint8_t* cache, int64_t num_slots, hipStream_t stream);
+hipError_t launch_kv_channel_scales(const void* kv, int dtype, int64_t T, int64_t C, int64_t ldkv, int fmt,
+                                    float* scales, void* ws, hipStream_t stream);
+hipError_t launch_kv_quantize_paged(const void* kv, int dtype, int64_t T, int64_t C, int64_t ldkv, const float* scales,
+                                    int fmt, const int32_t* slot, uint8_t* cache, int64_t num_slots,
+                                    hipStream_t stream);
 hipError_t launch_kv_dequantize_paged(const uint8_t* cache, int64_t num_slots, const int32_t* slot, int64_t T,
-                                      int64_t C, const float* scales, int fmt, float* out, int64_t ldo,
+                                      int64_t C, const float* scales, int fmt, void* out, int out_dtype, int64_t ldo,
                                       hipStream_t stream);
 
 // The dense GEMM launchers write BF16 y, or, when y32 is not null, the fp32

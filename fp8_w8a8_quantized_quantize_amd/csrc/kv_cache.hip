@@ -10,10 +10,14 @@
 // token's row goes (512K-context page, §3.3).
 //
 // All three kernels are HBM-bound streams.  A thread owns four adjacent
-// channels (one float4 of a row, one 32-bit word of codes) and walks down a
-// range of rows, so a wave touches 1 KB of fp32 or 256 B of codes per row,
-// contiguous, and the per-channel scale and its reciprocal are formed once
-// per thread, not per element.  The fp32 stream that is read once (the
+// channels (16 bytes of an fp32 row or 8 of a bf16 / fp16 row, one 32-bit word
+// of codes) and walks down a range of rows, so a wave touches contiguous
+// memory per row, and the per-channel scale and its reciprocal are formed
+// once per thread, not per element.  KV rows may arrive as fp32, bf16 or
+// fp16 (the pages convert FP16 KV to FP8; 512K-context page, §3.3); a
+// 16-bit value converts to fp32 exactly, so the codes depend only on the
+// value.  The read back is written as fp32, bf16 or fp16, rounded to
+// nearest even from the fp32 product.  The fp32 stream that is read once (the
 // batch) and the one that is written once (the read back) go through
 // nontemporal loads and stores: measured on MI355X they lift the batch read
 // from about 5.4 to 6.4 TB/s and the read back from 4.6 to 6.7 TB/s.
@@ -37,6 +41,72 @@ __device__ __forceinline__ float4 load_nt(const float4* p) {
 __device__ __forceinline__ void store_nt(const float4& v, float4* p) {
     const v4f t = {v.x, v.y, v.z, v.w};
     __builtin_nontemporal_store(t, reinterpret_cast<v4f*>(p));
+}
+
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float half_to_float(uint32_t h) {
+    _Float16 f;
+    const uint16_t b = (uint16_t)h;
+    __builtin_memcpy(&f, &b, 2);
+    return (float)f;
+}
+
+__device__ __forceinline__ uint32_t float_to_half_bits(float x) {
+    const _Float16 f = (_Float16)x;  // round to nearest even
+    uint16_t b;
+    __builtin_memcpy(&b, &f, 2);
+    return b;
+}
+
+// Quads (4 consecutive channels) per thread: one 16-byte load covers 4
+// fp32 or 8 bf16 / fp16 channels.
+template <int DT>
+constexpr int kv_quads() {
+    return DT == kKvF32 ? 1 : 2;
+}
+
+// The 4 * Q elements of a KV row at element offset `e` from `base`, as fp32
+// quads; DT: kKvF32, kKvBF16 or kKvF16.  Read once: nontemporal.
+template <int DT>
+__device__ __forceinline__ void kv_load(const void* base, int64_t e, float4 (&v)[kv_quads<DT>()]) {
+    if constexpr (DT == kKvF32) {
+        v[0] = load_nt(reinterpret_cast<const float4*>(static_cast<const float*>(base) + e));
+    } else {
+        const v4u w = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(static_cast<const uint16_t*>(base) + e));
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const uint32_t a = w[2 * q], b = w[2 * q + 1];
+            if constexpr (DT == kKvBF16)
+                v[q] = make_float4(__uint_as_float(a << 16), __uint_as_float(a & 0xFFFF0000u), __uint_as_float(b << 16),
+                                   __uint_as_float(b & 0xFFFF0000u));
+            else
+                v[q] = make_float4(half_to_float(a & 0xFFFFu), half_to_float(a >> 16), half_to_float(b & 0xFFFFu),
+                                   half_to_float(b >> 16));
+        }
+    }
+}
+
+// 4 * Q fp32 values to consecutive output elements (written once).
+template <int DT>
+__device__ __forceinline__ void kv_store(void* base, int64_t e, const float4 (&v)[kv_quads<DT>()]) {
+    if constexpr (DT == kKvF32) {
+        store_nt(v[0], reinterpret_cast<float4*>(static_cast<float*>(base) + e));
+    } else {
+        v4u w;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            if constexpr (DT == kKvBF16) {
+                w[2 * q] = pack_bf16x2(v[q].x, v[q].y);
+                w[2 * q + 1] = pack_bf16x2(v[q].z, v[q].w);
+            } else {
+                w[2 * q] = float_to_half_bits(v[q].x) | (float_to_half_bits(v[q].y) << 16);
+                w[2 * q + 1] = float_to_half_bits(v[q].z) | (float_to_half_bits(v[q].w) << 16);
+            }
+        }
+        __builtin_nontemporal_store(w, reinterpret_cast<v4u*>(static_cast<uint16_t*>(base) + e));
+    }
 }
 
 // Two fp32 -> FP8 codes in bytes [2*HI, 2*HI+1] of `old`, clamped to the
@@ -73,28 +143,40 @@ __device__ __forceinline__ float4 abs_max4(float4 m, const float4& v) {
 }
 
 // Column |x| maxima of one chunk of rows: grid.x spans the channel groups,
-// grid.y the row chunks.  The partial of chunk k for channel group g goes to
-// part[g * chunks + k], so the reduction reads each group's partials
-// contiguously.
-__global__ __launch_bounds__(kKvThreads) void kv_amax_partial(const float* __restrict__ kv, int64_t ld4, int T,
-                                                              int C4, int rows_per_chunk, int chunks,
+// grid.y the row chunks.  The partial of chunk k for quad G (channels 4G ..
+// 4G + 3) goes to part[G * chunks + k], so the reduction reads each quad's
+// partials contiguously.
+template <int DT>
+__global__ __launch_bounds__(kKvThreads) void kv_amax_partial(const void* __restrict__ kv, int64_t ld, int T,
+                                                              int CQ, int rows_per_chunk, int chunks,
                                                               float4* __restrict__ part) {
-    const int g = blockIdx.x * kKvThreads + threadIdx.x;
-    if (g >= C4) return;
+    constexpr int Q = kv_quads<DT>();
+    const int g = blockIdx.x * kKvThreads + threadIdx.x;  // channels [4Qg, 4Qg + 4Q)
+    if (g >= CQ) return;
     const int r0 = blockIdx.y * rows_per_chunk;
     const int r1 = min(T, r0 + rows_per_chunk);
-    const float4* p = reinterpret_cast<const float4*>(kv) + g;
-    float4 m = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    const int64_t e0 = 4 * Q * (int64_t)g;
+    float4 m[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) m[q] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     int r = r0;
     for (; r + kKvUnroll <= r1; r += kKvUnroll) {
-        float4 v[kKvUnroll];
+        float4 v[kKvUnroll][Q];
 #pragma unroll
-        for (int i = 0; i < kKvUnroll; ++i) v[i] = load_nt(p + (int64_t)(r + i) * ld4);
+        for (int i = 0; i < kKvUnroll; ++i) kv_load<DT>(kv, (int64_t)(r + i) * ld + e0, v[i]);
 #pragma unroll
-        for (int i = 0; i < kKvUnroll; ++i) m = abs_max4(m, v[i]);
+        for (int i = 0; i < kKvUnroll; ++i)
+#pragma unroll
+            for (int q = 0; q < Q; ++q) m[q] = abs_max4(m[q], v[i][q]);
     }
-    for (; r < r1; ++r) m = abs_max4(m, load_nt(p + (int64_t)r * ld4));
-    part[(int64_t)g * chunks + blockIdx.y] = m;
+    for (; r < r1; ++r) {
+        float4 v[Q];
+        kv_load<DT>(kv, (int64_t)r * ld + e0, v);
+#pragma unroll
+        for (int q = 0; q < Q; ++q) m[q] = abs_max4(m[q], v[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < Q; ++q) part[((int64_t)Q * g + q) * chunks + blockIdx.y] = m[q];
 }
 
 // One wave per channel group: the 64 lanes stride over the chunks' partials,
@@ -136,78 +218,128 @@ __device__ __forceinline__ uint32_t kv_encode4(const float4& v, const RowScale (
     return (uint32_t)w;
 }
 
+// fl32(d * s) per element.  The product must be rounded to fp32 before any
+// narrowing store: left to itself the compiler fuses the multiply and the
+// fp16 conversion into one mixed-precision FMA (a single rounding, and
+// -0 * s + 0 = +0), which changes fp16 results; the empty asm pins each
+// product in a register as an fp32 value.
+__device__ __forceinline__ float4 scale4(const float4& d, const float4& s) {
+    float4 p = make_float4(d.x * s.x, d.y * s.y, d.z * s.z, d.w * s.w);
+    asm volatile("" : "+v"(p.x), "+v"(p.y), "+v"(p.z), "+v"(p.w));
+    return p;
+}
+
 // Rows [r0, r1) of the batch into their cache slots.  Tokens whose slot is
 // outside [0, num_slots) are skipped.
-template <int FMT>
-__global__ __launch_bounds__(kKvThreads) void kv_quantize_paged(const float* __restrict__ kv, int64_t ld4,
+template <int FMT, int DT>
+__global__ __launch_bounds__(kKvThreads) void kv_quantize_paged(const void* __restrict__ kv, int64_t ld,
                                                                 const float* __restrict__ scales,
                                                                 const int32_t* __restrict__ slot,
                                                                 uint8_t* __restrict__ cache, int64_t num_slots, int T,
-                                                                int C4, int rows_per_block) {
+                                                                int CQ, int rows_per_block) {
+    constexpr int Q = kv_quads<DT>();
+    constexpr int U = kKvQuantUnroll / Q;  // rows in flight: 16 (fp32) or 8 (16-bit, 16 channels each)
     const int g = blockIdx.x * kKvThreads + threadIdx.x;
-    if (g >= C4) return;
-    const float4 s4 = reinterpret_cast<const float4*>(scales)[g];
-    const RowScale rs[4] = {channel_scale(s4.x), channel_scale(s4.y), channel_scale(s4.z), channel_scale(s4.w)};
+    if (g >= CQ) return;
+    RowScale rs[Q][4];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        const float4 s4 = reinterpret_cast<const float4*>(scales)[Q * g + q];
+        rs[q][0] = channel_scale(s4.x);
+        rs[q][1] = channel_scale(s4.y);
+        rs[q][2] = channel_scale(s4.z);
+        rs[q][3] = channel_scale(s4.w);
+    }
     const int r0 = blockIdx.y * rows_per_block;
     const int r1 = min(T, r0 + rows_per_block);
-    const float4* p = reinterpret_cast<const float4*>(kv) + g;
-    uint32_t* out = reinterpret_cast<uint32_t*>(cache) + g;
-    const int64_t c4 = C4;
+    const int64_t e0 = 4 * Q * (int64_t)g;
+    const int64_t C = 4 * Q * (int64_t)CQ;  // cache row length in bytes
+    auto put = [&](int s, const float4 (&v)[Q]) {
+        uint8_t* dst = cache + (int64_t)s * C + e0;
+        if constexpr (Q == 1) {
+            *reinterpret_cast<uint32_t*>(dst) = kv_encode4<FMT>(v[0], rs[0]);
+        } else {
+            v2u w;
+            w[0] = kv_encode4<FMT>(v[0], rs[0]);
+            w[1] = kv_encode4<FMT>(v[1], rs[1]);
+            *reinterpret_cast<v2u*>(dst) = w;
+        }
+    };
     int r = r0;
-    for (; r + kKvQuantUnroll <= r1; r += kKvQuantUnroll) {
-        float4 v[kKvQuantUnroll];
-        int sl[kKvQuantUnroll];
+    for (; r + U <= r1; r += U) {
+        float4 v[U][Q];
+        int sl[U];
 #pragma unroll
-        for (int i = 0; i < kKvQuantUnroll; ++i) {
+        for (int i = 0; i < U; ++i) {
             sl[i] = slot[r + i];
-            v[i] = load_nt(p + (int64_t)(r + i) * ld4);
+            kv_load<DT>(kv, (int64_t)(r + i) * ld + e0, v[i]);
         }
 #pragma unroll
-        for (int i = 0; i < kKvQuantUnroll; ++i)
-            if (sl[i] >= 0 && sl[i] < num_slots) out[(int64_t)sl[i] * c4] = kv_encode4<FMT>(v[i], rs);
+        for (int i = 0; i < U; ++i)
+            if (sl[i] >= 0 && sl[i] < num_slots) put(sl[i], v[i]);
     }
     for (; r < r1; ++r) {
         const int s = slot[r];
-        if (s >= 0 && s < num_slots) out[(int64_t)s * c4] = kv_encode4<FMT>(load_nt(p + (int64_t)r * ld4), rs);
+        if (s >= 0 && s < num_slots) {
+            float4 v[Q];
+            kv_load<DT>(kv, (int64_t)r * ld + e0, v);
+            put(s, v);
+        }
     }
 }
 
 // out[t, :] = decoded cache row slot[t] times the channel scales; a slot
 // outside [0, num_slots) reads as code 0, so its row is all +0.
-template <int FMT>
+template <int FMT, int DT>
 __global__ __launch_bounds__(kKvThreads) void kv_dequantize_paged(const uint8_t* __restrict__ cache, int64_t num_slots,
                                                                   const int32_t* __restrict__ slot,
                                                                   const float* __restrict__ scales,
-                                                                  float* __restrict__ outp, int64_t ldo4, int T,
-                                                                  int C4, int rows_per_block) {
+                                                                  void* __restrict__ out, int64_t ldo, int T,
+                                                                  int CQ, int rows_per_block) {
+    constexpr int Q = kv_quads<DT>();
     const int g = blockIdx.x * kKvThreads + threadIdx.x;
-    if (g >= C4) return;
-    float4 s = reinterpret_cast<const float4*>(scales)[g];
-    s = make_float4(fmaxf(s.x, kScaleFloor), fmaxf(s.y, kScaleFloor), fmaxf(s.z, kScaleFloor), fmaxf(s.w, kScaleFloor));
+    if (g >= CQ) return;
+    float4 s[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        const float4 t = reinterpret_cast<const float4*>(scales)[Q * g + q];
+        s[q] = make_float4(fmaxf(t.x, kScaleFloor), fmaxf(t.y, kScaleFloor), fmaxf(t.z, kScaleFloor),
+                           fmaxf(t.w, kScaleFloor));
+    }
     const int r0 = blockIdx.y * rows_per_block;
     const int r1 = min(T, r0 + rows_per_block);
-    const uint32_t* in = reinterpret_cast<const uint32_t*>(cache) + g;
-    float4* out = reinterpret_cast<float4*>(outp) + g;
-    const int64_t c4 = C4;
+    const int64_t e0 = 4 * Q * (int64_t)g;
+    const int64_t C = 4 * Q * (int64_t)CQ;
+    auto fetch = [&](int r, uint32_t (&w)[Q]) {
+        const int sl = slot[r];
+        const bool ok = sl >= 0 && sl < num_slots;
+        const uint8_t* src = cache + (int64_t)(ok ? sl : 0) * C + e0;
+        if constexpr (Q == 1) {
+            w[0] = ok ? *reinterpret_cast<const uint32_t*>(src) : 0u;
+        } else {
+            const v2u t = ok ? *reinterpret_cast<const v2u*>(src) : v2u{0u, 0u};
+            w[0] = t[0];
+            w[1] = t[1];
+        }
+    };
+    auto emit = [&](int r, const uint32_t (&w)[Q]) {
+        float4 o[Q];
+#pragma unroll
+        for (int q = 0; q < Q; ++q) o[q] = scale4(kv_decode4<FMT>(w[q]), s[q]);
+        kv_store<DT>(out, (int64_t)r * ldo + e0, o);
+    };
     int r = r0;
     for (; r + kKvUnroll <= r1; r += kKvUnroll) {
-        uint32_t w[kKvUnroll];
+        uint32_t w[kKvUnroll][Q];
 #pragma unroll
-        for (int i = 0; i < kKvUnroll; ++i) {
-            const int sl = slot[r + i];
-            w[i] = (sl >= 0 && sl < num_slots) ? in[(int64_t)sl * c4] : 0u;
-        }
+        for (int i = 0; i < kKvUnroll; ++i) fetch(r + i, w[i]);
 #pragma unroll
-        for (int i = 0; i < kKvUnroll; ++i) {
-            const float4 d = kv_decode4<FMT>(w[i]);
-            store_nt(make_float4(d.x * s.x, d.y * s.y, d.z * s.z, d.w * s.w), out + (int64_t)(r + i) * ldo4);
-        }
+        for (int i = 0; i < kKvUnroll; ++i) emit(r + i, w[i]);
     }
     for (; r < r1; ++r) {
-        const int sl = slot[r];
-        const uint32_t w = (sl >= 0 && sl < num_slots) ? in[(int64_t)sl * c4] : 0u;
-        const float4 d = kv_decode4<FMT>(w);
-        store_nt(make_float4(d.x * s.x, d.y * s.y, d.z * s.z, d.w * s.w), out + (int64_t)r * ldo4);
+        uint32_t w[Q];
+        fetch(r, w);
+        emit(r, w);
     }
 }
 
@@ -235,22 +367,39 @@ int64_t rows_per_block(int64_t T, int64_t col_blocks, int64_t target) {
 
 }  // namespace
 
-KvChunks kv_amax_chunks(int64_t T, int64_t C) {
-    const int64_t col_blocks = ceil_div(C / 4, kKvThreads);
+// Row chunks of the channel-maxima pass for rows read `quads` channel quads
+// per thread (1 for fp32, 2 for 16-bit elements).
+KvChunks kv_amax_chunks(int64_t T, int64_t C, int quads) {
+    const int64_t col_blocks = ceil_div(C / 4 / quads, kKvThreads);
     const int64_t rpc = rows_per_block(T, std::max<int64_t>(col_blocks, 1), kKvAmaxBlocks);
     return KvChunks{(int)rpc, (int)std::max<int64_t>(1, ceil_div(T, rpc))};
 }
 
-size_t kv_scales_ws_bytes(int64_t T, int64_t C) { return (size_t)kv_amax_chunks(T, C).chunks * (size_t)C * 4; }
+// Sized for the element type with the most chunks (the 16-bit one).
+size_t kv_scales_ws_bytes(int64_t T, int64_t C) { return (size_t)kv_amax_chunks(T, C, 2).chunks * (size_t)C * 4; }
 
-hipError_t launch_kv_channel_scales(const float* kv, int64_t T, int64_t C, int64_t ldkv, int fmt, float* scales,
-                                    void* ws, hipStream_t stream) {
+// Dispatch on the element type (DT) and the code format (FMT).
+#define FP8K_KV_DT(dt, CALL)                 \
+    switch (dt) {                            \
+        case kKvBF16: CALL(kKvBF16); break;  \
+        case kKvF16: CALL(kKvF16); break;    \
+        default: CALL(kKvF32); break;        \
+    }
+
+hipError_t launch_kv_channel_scales(const void* kv, int dtype, int64_t T, int64_t C, int64_t ldkv, int fmt,
+                                    float* scales, void* ws, hipStream_t stream) {
     const int C4 = (int)(C / 4);
-    const KvChunks ch = kv_amax_chunks(T, C);
+    const KvChunks ch = kv_amax_chunks(T, C, dtype == kKvF32 ? 1 : 2);
     float4* part = static_cast<float4*>(ws);
-    const dim3 g1((unsigned)ceil_div(C4, kKvThreads), (unsigned)ch.chunks);
-    hipLaunchKernelGGL(kv_amax_partial, g1, dim3(kKvThreads), 0, stream, kv, ldkv / 4, (int)T, C4, ch.rows_per_chunk,
-                       ch.chunks, part);
+#define FP8K_KV_AMAX(D)                                                                                              \
+    {                                                                                                                \
+        const int cq = C4 / kv_quads<D>();                                                                           \
+        const dim3 g1((unsigned)ceil_div(cq, kKvThreads), (unsigned)ch.chunks);                                      \
+        hipLaunchKernelGGL(kv_amax_partial<D>, g1, dim3(kKvThreads), 0, stream, kv, ldkv, (int)T, cq, ch.rows_per_chunk, \
+                           ch.chunks, part);                                                                         \
+    }
+    FP8K_KV_DT(dtype, FP8K_KV_AMAX)
+#undef FP8K_KV_AMAX
     const dim3 g2((unsigned)ceil_div(C4, kKvThreads / kWave));
     if (fmt == kKvE5M2)
         hipLaunchKernelGGL(kv_scale_finish<kKvE5M2>, g2, dim3(kKvThreads), 0, stream, part, ch.chunks, C4,
@@ -261,35 +410,49 @@ hipError_t launch_kv_channel_scales(const float* kv, int64_t T, int64_t C, int64
     return hipGetLastError();
 }
 
-hipError_t launch_kv_quantize_paged(const float* kv, int64_t T, int64_t C, int64_t ldkv, const float* scales, int fmt,
-                                    const int32_t* slot, uint8_t* cache, int64_t num_slots, hipStream_t stream) {
+hipError_t launch_kv_quantize_paged(const void* kv, int dtype, int64_t T, int64_t C, int64_t ldkv, const float* scales,
+                                    int fmt, const int32_t* slot, uint8_t* cache, int64_t num_slots,
+                                    hipStream_t stream) {
     const int C4 = (int)(C / 4);
-    const int64_t cb = ceil_div(C4, kKvThreads);
-    const int64_t rpb = rows_per_block(T, cb, kKvTargetBlocks);
-    const dim3 grid((unsigned)cb, (unsigned)ceil_div(T, rpb));
-    if (fmt == kKvE5M2)
-        hipLaunchKernelGGL(kv_quantize_paged<kKvE5M2>, grid, dim3(kKvThreads), 0, stream, kv, ldkv / 4, scales, slot,
-                           cache, num_slots, (int)T, C4, (int)rpb);
-    else
-        hipLaunchKernelGGL(kv_quantize_paged<kKvE4M3>, grid, dim3(kKvThreads), 0, stream, kv, ldkv / 4, scales, slot,
-                           cache, num_slots, (int)T, C4, (int)rpb);
+#define FP8K_KV_Q(D)                                                                                                   \
+    {                                                                                                                  \
+        const int cq = C4 / kv_quads<D>();                                                                             \
+        const int64_t cb = ceil_div(cq, kKvThreads);                                                                   \
+        const int64_t rpb = rows_per_block(T, cb, kKvTargetBlocks);                                                    \
+        const dim3 grid((unsigned)cb, (unsigned)ceil_div(T, rpb));                                                     \
+        if (fmt == kKvE5M2)                                                                                            \
+            hipLaunchKernelGGL((kv_quantize_paged<kKvE5M2, D>), grid, dim3(kKvThreads), 0, stream, kv, ldkv, scales,    \
+                               slot, cache, num_slots, (int)T, cq, (int)rpb);                                          \
+        else                                                                                                           \
+            hipLaunchKernelGGL((kv_quantize_paged<kKvE4M3, D>), grid, dim3(kKvThreads), 0, stream, kv, ldkv, scales,    \
+                               slot, cache, num_slots, (int)T, cq, (int)rpb);                                          \
+    }
+    FP8K_KV_DT(dtype, FP8K_KV_Q)
+#undef FP8K_KV_Q
     return hipGetLastError();
 }
 
 hipError_t launch_kv_dequantize_paged(const uint8_t* cache, int64_t num_slots, const int32_t* slot, int64_t T,
-                                      int64_t C, const float* scales, int fmt, float* out, int64_t ldo,
+                                      int64_t C, const float* scales, int fmt, void* out, int out_dtype, int64_t ldo,
                                       hipStream_t stream) {
     const int C4 = (int)(C / 4);
-    const int64_t cb = ceil_div(C4, kKvThreads);
-    const int64_t rpb = rows_per_block(T, cb, kKvTargetBlocks);
-    const dim3 grid((unsigned)cb, (unsigned)ceil_div(T, rpb));
-    if (fmt == kKvE5M2)
-        hipLaunchKernelGGL(kv_dequantize_paged<kKvE5M2>, grid, dim3(kKvThreads), 0, stream, cache, num_slots, slot,
-                           scales, out, ldo / 4, (int)T, C4, (int)rpb);
-    else
-        hipLaunchKernelGGL(kv_dequantize_paged<kKvE4M3>, grid, dim3(kKvThreads), 0, stream, cache, num_slots, slot,
-                           scales, out, ldo / 4, (int)T, C4, (int)rpb);
+#define FP8K_KV_DQ(D)                                                                                                  \
+    {                                                                                                                  \
+        const int cq = C4 / kv_quads<D>();                                                                             \
+        const int64_t cb = ceil_div(cq, kKvThreads);                                                                   \
+        const int64_t rpb = rows_per_block(T, cb, kKvTargetBlocks);                                                    \
+        const dim3 grid((unsigned)cb, (unsigned)ceil_div(T, rpb));                                                     \
+        if (fmt == kKvE5M2)                                                                                            \
+            hipLaunchKernelGGL((kv_dequantize_paged<kKvE5M2, D>), grid, dim3(kKvThreads), 0, stream, cache, num_slots,  \
+                               slot, scales, out, ldo, (int)T, cq, (int)rpb);                                          \
+        else                                                                                                           \
+            hipLaunchKernelGGL((kv_dequantize_paged<kKvE4M3, D>), grid, dim3(kKvThreads), 0, stream, cache, num_slots,  \
+                               slot, scales, out, ldo, (int)T, cq, (int)rpb);                                          \
+    }
+    FP8K_KV_DT(out_dtype, FP8K_KV_DQ)
+#undef FP8K_KV_DQ
     return hipGetLastError();
 }
+#undef FP8K_KV_DT
 
 }  // namespace fp8k

@@ -265,18 +265,21 @@ size_t fp8_mx_workspace_bytes(int64_t M, int64_t N, int64_t K);
  * deployment page, §2.3: the E4M3 KV variant and its absmax/448 scale).
  *
  * A KV batch is T token rows of C channels (e.g. the K and V heads of one
- * layer side by side, or one latent vector): kv fp32 [T, C], row stride
- * ldkv.  The cache is a pool of num_slots rows of C codes (u8 [num_slots, C],
+ * layer side by side, or one latent vector): kv [T, C] of fp32, bf16 or
+ * fp16 elements (kv_dtype; 16-bit values convert to fp32 exactly, and all
+ * arithmetic below is on that fp32 value), row stride ldkv elements.  The cache is a pool of num_slots rows of C codes (u8 [num_slots, C],
  * unit-stride rows of exactly C bytes); slot_mapping int32 [T] names each
  * token's row, physical block * block size + offset in the block, as the
  * caller's block table resolves it.  fmt picks the code format; scales are
  * fp32 [C], one per channel, floored at 1e-12f wherever they are used.
- * C must be a multiple of 4; kv and out row strides multiples of 4
- * elements; kv, scales, cache, out 16-byte aligned (else
- * FP8_ERR_UNSUPPORTED).  T, C, num_slots <= 2^31 - 1.  Inputs are assumed
- * finite.
+ * C must be a multiple of 4 (of 8 for bf16 / fp16 rows, which are read
+ * 8 channels at a time); kv and out rows 16-byte aligned (row stride
+ * times element size a multiple of 16 bytes); kv, scales, cache, out
+ * 16-byte aligned (else FP8_ERR_UNSUPPORTED).  T, C, num_slots <= 2^31 - 1.
+ * Inputs are assumed finite.
  */
 typedef enum { FP8_KV_E4M3 = 0, FP8_KV_E5M2 = 1 } fp8_kv_format_t;
+typedef enum { FP8_KV_F32 = 0, FP8_KV_BF16 = 1, FP8_KV_F16 = 2 } fp8_kv_dtype_t;
 
 /*
  * Per-channel scales of a KV batch (the online calibration of the Llama 3
@@ -285,8 +288,9 @@ typedef enum { FP8_KV_E4M3 = 0, FP8_KV_E5M2 = 1 } fp8_kv_format_t;
  * fmt_max = 448 (E4M3) or 57344 (E5M2).  T == 0 gives the floor.  ws: at
  * least fp8_kv_scales_workspace_bytes(T, C) bytes, 16-byte aligned.
  */
-fp8_status_t fp8_kv_channel_scales(const float* kv, int64_t T, int64_t C, int64_t ldkv, fp8_kv_format_t fmt,
-                                   float* scales, void* ws, size_t ws_bytes, hipStream_t stream);
+fp8_status_t fp8_kv_channel_scales(const void* kv, fp8_kv_dtype_t kv_dtype, int64_t T, int64_t C, int64_t ldkv,
+                                   fp8_kv_format_t fmt, float* scales, void* ws, size_t ws_bytes,
+                                   hipStream_t stream);
 
 /* Workspace bytes fp8_kv_channel_scales needs (host only; SIZE_MAX for
  * invalid sizes). */
@@ -301,19 +305,20 @@ size_t fp8_kv_scales_workspace_bytes(int64_t T, int64_t C);
  * as they were.  Two tokens naming the same slot race (one of them wins).
  * No workspace.
  */
-fp8_status_t fp8_kv_quantize_paged(const float* kv, int64_t T, int64_t C, int64_t ldkv, const float* scales,
-                                   fp8_kv_format_t fmt, const int32_t* slot_mapping, uint8_t* cache,
-                                   int64_t num_slots, hipStream_t stream);
+fp8_status_t fp8_kv_quantize_paged(const void* kv, fp8_kv_dtype_t kv_dtype, int64_t T, int64_t C, int64_t ldkv,
+                                   const float* scales, fp8_kv_format_t fmt, const int32_t* slot_mapping,
+                                   uint8_t* cache, int64_t num_slots, hipStream_t stream);
 
 /*
  * Read a sequence's rows back out of the cache:
- *   out[t,c] = fl32(dec_fmt(cache[slot_mapping[t], c]) * scales[c])
- * out fp32 [T, C], row stride ldo; a slot outside [0, num_slots) gives a
- * row of +0.  No workspace.
+ *   out[t,c] = round_out(fl32(dec_fmt(cache[slot_mapping[t], c]) * scales[c]))
+ * out [T, C] of out_dtype elements (fp32: the product itself; bf16 / fp16:
+ * rounded to nearest even), row stride ldo elements; a slot outside
+ * [0, num_slots) gives a row of +0.  No workspace.
  */
 fp8_status_t fp8_kv_dequantize_paged(const uint8_t* cache, int64_t num_slots, const int32_t* slot_mapping,
-                                     int64_t T, int64_t C, const float* scales, fp8_kv_format_t fmt, float* out,
-                                     int64_t ldo, hipStream_t stream);
+                                     int64_t T, int64_t C, const float* scales, fp8_kv_format_t fmt, void* out,
+                                     fp8_kv_dtype_t out_dtype, int64_t ldo, hipStream_t stream);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char* fp8_status_string(fp8_status_t status);

@@ -146,9 +146,9 @@ WORKLOADS = {
                                desc="Llama-3-70B prefill square GEMM M=N=K=8192 with fused quantize"),
     "moe-64x2048x7168": dict(kind="moe", T=4096, E=64, topk=8, zipf=1.1, K=7168, N=2048, n_out=None,
                              mult=50.0, desc="MoE 64 experts K=7168 N=2048, 4096 tokens top-8 Zipf(1.1)"),
-    "kv-llama3-70b-32k": dict(kind="kv", T=32768, C=2048, block=16, fmt="e5m2",
+    "kv-llama3-70b-32k": dict(kind="kv", T=32768, C=2048, block=16, fmt="e5m2", dtype="bf16",
                               desc="Llama-3-70B KV cache, one layer (8 KV heads x 128, K and V), "
-                                   "32768-token prefill into 16-token pages, E5M2"),
+                                   "32768-token prefill of bf16 rows into 16-token pages, E5M2"),
 }
 
 

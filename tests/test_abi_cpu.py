@@ -240,40 +240,49 @@ def test_kv_validation():
     L = fp8.lib()
     E4, E5 = fp8.FP8_KV_E4M3, fp8.FP8_KV_E5M2
     # workspace: one fp32 partial maximum per channel and row chunk (about 256 workgroups in all)
-    assert L.fp8_kv_scales_workspace_bytes(32768, 2048) == 128 * 2048 * 4
+    assert L.fp8_kv_scales_workspace_bytes(32768, 2048) == 256 * 2048 * 4   # 16-bit rows: 1 column block
     assert L.fp8_kv_scales_workspace_bytes(32768, 576) == 256 * 576 * 4
     assert L.fp8_kv_scales_workspace_bytes(0, 576) == 576 * 4          # one chunk; 2304 = 9 * 256
     assert L.fp8_kv_scales_workspace_bytes(0, 68) == 512              # rounded up to 256 bytes
     assert L.fp8_kv_scales_workspace_bytes(10, 6) == ctypes.c_size_t(-1).value     # C % 4
     assert L.fp8_kv_scales_workspace_bytes(-1, 8) == ctypes.c_size_t(-1).value
     wsb = L.fp8_kv_scales_workspace_bytes(64, 128)
-    # kv, T, C, ldkv, fmt, scales, ws, ws_bytes, stream
-    assert L.fp8_kv_channel_scales(P, 64, 128, 128, E5, Q, P, wsb - 1, S0) == FP8_ERR_WORKSPACE
-    assert L.fp8_kv_channel_scales(P, 64, 128, 128, 2, Q, P, wsb, S0) == FP8_ERR_INVALID_ARGUMENT  # format
-    assert L.fp8_kv_channel_scales(P, 64, 130, 132, E5, Q, P, wsb, S0) == FP8_ERR_UNSUPPORTED      # C % 4
-    assert L.fp8_kv_channel_scales(P, 64, 128, 126, E5, Q, P, wsb, S0) == FP8_ERR_INVALID_ARGUMENT  # ldkv < C
-    assert L.fp8_kv_channel_scales(P, 64, 128, 130, E5, Q, P, wsb, S0) == FP8_ERR_UNSUPPORTED      # ldkv % 4
-    assert L.fp8_kv_channel_scales(P, 64, 128, 128, E5, MIS, P, wsb, S0) == FP8_ERR_UNSUPPORTED
-    assert L.fp8_kv_channel_scales(P, 64, 128, 128, E5, Q, 0, wsb, S0) == FP8_ERR_INVALID_ARGUMENT
-    assert L.fp8_kv_channel_scales(P, 64, 128, 128, E5, Q, MIS, wsb, S0) == FP8_ERR_UNSUPPORTED
-    assert L.fp8_kv_channel_scales(0, 0, 0, 0, E4, 0, 0, 0, S0) == FP8_OK                           # empty
-    # kv, T, C, ldkv, scales, fmt, slot, cache, num_slots, stream
-    assert L.fp8_kv_quantize_paged(P, 8, 64, 64, Q, E5, P, Q, -1, S0) == FP8_ERR_INVALID_ARGUMENT
-    assert L.fp8_kv_quantize_paged(P, 8, 64, 64, Q, E5, 0, Q, 16, S0) == FP8_ERR_INVALID_ARGUMENT   # no slots
-    assert L.fp8_kv_quantize_paged(P, 8, 64, 64, Q, E5, P + 2, Q, 16, S0) == FP8_ERR_UNSUPPORTED
-    assert L.fp8_kv_quantize_paged(P, 8, 64, 64, Q, E5, P, MIS, 16, S0) == FP8_ERR_UNSUPPORTED      # cache
-    assert L.fp8_kv_quantize_paged(P, 8, 64, 64, Q, 7, P, Q, 16, S0) == FP8_ERR_INVALID_ARGUMENT
-    assert L.fp8_kv_quantize_paged(P, 8, 64, 64, Q, E5, P, Q, 1 << 31, S0) == FP8_ERR_UNSUPPORTED
-    assert L.fp8_kv_quantize_paged(P, 8, 64, 64, Q, E5, P, 0, 16, S0) == FP8_ERR_INVALID_ARGUMENT
-    assert L.fp8_kv_quantize_paged(P, 8, 64, 64, Q, E5, P, Q, 0, S0) == FP8_OK    # nothing to write into
-    assert L.fp8_kv_quantize_paged(0, 0, 64, 64, 0, E5, 0, Q, 16, S0) == FP8_OK
-    # cache, num_slots, slot, T, C, scales, fmt, out, ldo, stream
-    assert L.fp8_kv_dequantize_paged(Q, 16, P, 8, 64, Q, E5, P, 62, S0) == FP8_ERR_INVALID_ARGUMENT
-    assert L.fp8_kv_dequantize_paged(Q, 16, P, 8, 64, Q, E5, P, 66, S0) == FP8_ERR_UNSUPPORTED
-    assert L.fp8_kv_dequantize_paged(Q, 16, P, 8, 64, Q, E5, MIS, 64, S0) == FP8_ERR_UNSUPPORTED
-    assert L.fp8_kv_dequantize_paged(Q, 16, 0, 8, 64, Q, E5, P, 64, S0) == FP8_ERR_INVALID_ARGUMENT
-    assert L.fp8_kv_dequantize_paged(0, 16, P, 8, 64, Q, E5, P, 64, S0) == FP8_ERR_INVALID_ARGUMENT
-    assert L.fp8_kv_dequantize_paged(Q, 16, 0, 0, 64, Q, E5, 0, 64, S0) == FP8_OK
+    F32, BF16 = fp8.FP8_KV_F32, fp8.FP8_KV_BF16
+    # kv, dtype, T, C, ldkv, fmt, scales, ws, ws_bytes, stream
+    assert L.fp8_kv_channel_scales(P, F32, 64, 128, 128, E5, Q, P, wsb - 1, S0) == FP8_ERR_WORKSPACE
+    assert L.fp8_kv_channel_scales(P, F32, 64, 128, 128, 2, Q, P, wsb, S0) == FP8_ERR_INVALID_ARGUMENT  # format
+    assert L.fp8_kv_channel_scales(P, F32, 64, 130, 132, E5, Q, P, wsb, S0) == FP8_ERR_UNSUPPORTED      # C % 4
+    assert L.fp8_kv_channel_scales(P, F32, 64, 128, 126, E5, Q, P, wsb, S0) == FP8_ERR_INVALID_ARGUMENT  # ldkv < C
+    assert L.fp8_kv_channel_scales(P, F32, 64, 128, 130, E5, Q, P, wsb, S0) == FP8_ERR_UNSUPPORTED      # ldkv % 4
+    assert L.fp8_kv_channel_scales(P, F32, 64, 128, 128, E5, MIS, P, wsb, S0) == FP8_ERR_UNSUPPORTED
+    assert L.fp8_kv_channel_scales(P, F32, 64, 128, 128, E5, Q, 0, wsb, S0) == FP8_ERR_INVALID_ARGUMENT
+    assert L.fp8_kv_channel_scales(P, F32, 64, 128, 128, E5, Q, MIS, wsb, S0) == FP8_ERR_UNSUPPORTED
+    assert L.fp8_kv_channel_scales(0, F32, 0, 0, 0, E4, 0, 0, 0, S0) == FP8_OK                           # empty
+    # kv, dtype, T, C, ldkv, scales, fmt, slot, cache, num_slots, stream
+    assert L.fp8_kv_quantize_paged(P, F32, 8, 64, 64, Q, E5, P, Q, -1, S0) == FP8_ERR_INVALID_ARGUMENT
+    assert L.fp8_kv_quantize_paged(P, F32, 8, 64, 64, Q, E5, 0, Q, 16, S0) == FP8_ERR_INVALID_ARGUMENT   # no slots
+    assert L.fp8_kv_quantize_paged(P, F32, 8, 64, 64, Q, E5, P + 2, Q, 16, S0) == FP8_ERR_UNSUPPORTED
+    assert L.fp8_kv_quantize_paged(P, F32, 8, 64, 64, Q, E5, P, MIS, 16, S0) == FP8_ERR_UNSUPPORTED      # cache
+    assert L.fp8_kv_quantize_paged(P, F32, 8, 64, 64, Q, 7, P, Q, 16, S0) == FP8_ERR_INVALID_ARGUMENT
+    assert L.fp8_kv_quantize_paged(P, F32, 8, 64, 64, Q, E5, P, Q, 1 << 31, S0) == FP8_ERR_UNSUPPORTED
+    assert L.fp8_kv_quantize_paged(P, F32, 8, 64, 64, Q, E5, P, 0, 16, S0) == FP8_ERR_INVALID_ARGUMENT
+    assert L.fp8_kv_quantize_paged(P, F32, 8, 64, 64, Q, E5, P, Q, 0, S0) == FP8_OK    # nothing to write into
+    assert L.fp8_kv_quantize_paged(0, F32, 0, 64, 64, 0, E5, 0, Q, 16, S0) == FP8_OK
+    # element types: 16-bit rows need 16-byte row strides (multiples of 8 elements); unknown types are rejected
+    assert L.fp8_kv_channel_scales(P, BF16, 64, 128, 132, E5, Q, P, wsb, S0) == FP8_ERR_UNSUPPORTED   # 264 B rows
+    assert L.fp8_kv_channel_scales(P, 3, 64, 128, 128, E5, Q, P, wsb, S0) == FP8_ERR_INVALID_ARGUMENT
+    # 16-bit rows are read 8 channels at a time: C % 8 (C = 132 is fine for fp32 rows)
+    assert L.fp8_kv_channel_scales(P, BF16, 64, 132, 136, E5, Q, P, wsb, S0) == FP8_ERR_UNSUPPORTED
+    assert L.fp8_kv_quantize_paged(P, fp8.FP8_KV_F16, 8, 132, 136, Q, E5, P, Q, 16, S0) == FP8_ERR_UNSUPPORTED
+    assert L.fp8_kv_dequantize_paged(Q, 16, P, 8, 132, Q, E5, P, BF16, 136, S0) == FP8_ERR_UNSUPPORTED
+    assert L.fp8_kv_dequantize_paged(Q, 16, P, 8, 64, Q, E5, P, 5, 64, S0) == FP8_ERR_INVALID_ARGUMENT
+    # cache, num_slots, slot, T, C, scales, fmt, out, out_dtype, ldo, stream
+    assert L.fp8_kv_dequantize_paged(Q, 16, P, 8, 64, Q, E5, P, F32, 62, S0) == FP8_ERR_INVALID_ARGUMENT
+    assert L.fp8_kv_dequantize_paged(Q, 16, P, 8, 64, Q, E5, P, F32, 66, S0) == FP8_ERR_UNSUPPORTED
+    assert L.fp8_kv_dequantize_paged(Q, 16, P, 8, 64, Q, E5, MIS, F32, 64, S0) == FP8_ERR_UNSUPPORTED
+    assert L.fp8_kv_dequantize_paged(Q, 16, 0, 8, 64, Q, E5, P, F32, 64, S0) == FP8_ERR_INVALID_ARGUMENT
+    assert L.fp8_kv_dequantize_paged(0, 16, P, 8, 64, Q, E5, P, F32, 64, S0) == FP8_ERR_INVALID_ARGUMENT
+    assert L.fp8_kv_dequantize_paged(Q, 16, 0, 0, 64, Q, E5, 0, F32, 64, S0) == FP8_OK
 
 
 def test_mx_validation():

@@ -173,3 +173,41 @@ def test_overflowing_quotients_saturate(fmt, fid):
     top = 0x7B if fid == oracle.E5M2 else 0x7E
     assert (want[1, :5] & 0x7F).tolist() == [top] * 5
     assert_codes_equal(to_host(cache), want, f"{fmt} overflow")
+
+
+@pytest.mark.parametrize("fmt,fid", FMTS)
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_16bit_kv_rows_in_and_read_back_out(fmt, fid, dtype):
+    """KV rows in bf16 / fp16 (the converted fp32 value decides everything) and the
+    read back rounded to bf16 / fp16: scales, codes and output bits against the
+    oracle run on the same values."""
+    T, C, B, nb = 1500, 576, 16, 100
+    kv32 = synth.kv_activations(T, C, seed=41)
+    kv_d = torch.from_numpy(kv32).to(DEV).to(dtype)
+    kv_vals = kv_d.float().cpu().numpy()            # the exact values of the 16-bit rows
+    slot = synth.kv_slot_mapping(T, B, nb, seed=41)
+    slot[5] = -1
+    s = fp8.fp8_kv_channel_scales(kv_d, fmt)
+    s_want = oracle.kv_channel_scales(kv_vals, fid)
+    assert_scales_equal(to_host(s), s_want, f"{fmt} {dtype} scales")
+    cache = torch.zeros((nb * B, C), dtype=torch.uint8, device=DEV)
+    fp8.fp8_kv_quantize_paged(kv_d, s, to_dev(slot), cache, fmt)
+    c_want = oracle.kv_quantize(kv_vals, s_want, fid, slot, nb * B)
+    assert_codes_equal(to_host(cache), c_want, f"{fmt} {dtype} cache")
+    back32 = oracle.kv_dequantize(c_want, slot, s_want, fid)
+    out = fp8.fp8_kv_dequantize_paged(cache, to_dev(slot), s, fmt, out_dtype=dtype)
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    if dtype == torch.bfloat16:
+        want = oracle.bf16_from_double(back32.astype(np.float64))
+    else:
+        want = back32.astype(np.float16).view(np.uint16)
+    assert np.array_equal(got, want), f"{fmt} {dtype} read back"
+
+
+def test_16bit_strided_rows():
+    T, C, ld = 300, 512, 520
+    big = torch.from_numpy(synth.kv_activations(T, ld, seed=43)).to(DEV).to(torch.bfloat16)
+    view = big[:, :C]
+    s = fp8.fp8_kv_channel_scales(view, "e5m2")
+    vals = view.float().cpu().numpy()
+    assert_scales_equal(to_host(s), oracle.kv_channel_scales(vals, oracle.E5M2), "strided bf16")
