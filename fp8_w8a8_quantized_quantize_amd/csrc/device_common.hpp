@@ -92,12 +92,15 @@ __device__ __forceinline__ RowScale make_row_scale(float amax) {
 }
 
 // fl32(x / s) from r = RN(1 / s): q0 = RN(x r) is within one ulp of x / s,
-// the residual x - q0 s is exact in one FMA, and RN(q0 + residual * r) is
+// the residual q0 s - x is exact in one FMA, and RN(q0 - residual * r) is
 // then the correctly rounded quotient (Markstein's division theorem; a
 // reciprocal and two FMAs instead of a full IEEE division per element).  The
-// sign of x is put back so -0 stays -0.  Where x is subnormal the residual
-// can lose bits, but the quotient is then below 2^-11, whose E4M3 code is the
-// signed zero either way (E5M2's smallest step is 2^-16, so there too).
+// residual is taken as q0 s - x and subtracted, not as x - q0 s and added:
+// for x = -0 the former is +0 and q0 - (+0) r = -0, so signed zeros come out
+// right with no extra instruction (the other order gives +0 there).  Where x
+// is subnormal the residual can lose bits, but the quotient is then below
+// 2^-11, whose E4M3 code is the signed zero either way (E5M2's smallest step
+// is 2^-16, so there too), and its sign is still that of x.
 // q0 is clamped to +-2^20: when x * r overflows fp32 (a static or stale
 // scale far below |x| / 448) the residual would otherwise be inf - inf; a
 // clamped quotient is past every FP8 code and still saturates.  A CPU test
@@ -105,8 +108,8 @@ __device__ __forceinline__ RowScale make_row_scale(float amax) {
 // FP8-boundary quotients.
 __device__ __forceinline__ float div_by_scale(float x, const RowScale& rs) {
     const float q0 = __builtin_amdgcn_fmed3f(x * rs.r, -1048576.0f, 1048576.0f);
-    const float e = __builtin_fmaf(-q0, rs.s, x);
-    return __builtin_copysignf(__builtin_fmaf(e, rs.r, q0), x);
+    const float d = __builtin_fmaf(q0, rs.s, -x);
+    return __builtin_fmaf(d, -rs.r, q0);
 }
 
 __device__ __forceinline__ uint32_t cast4(const float4& v, const RowScale& rs) {

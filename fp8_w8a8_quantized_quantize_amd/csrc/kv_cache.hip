@@ -142,41 +142,66 @@ __device__ __forceinline__ float4 abs_max4(float4 m, const float4& v) {
     return make_float4(fmaxf(m.x, fabsf(v.x)), fmaxf(m.y, fabsf(v.y)), fmaxf(m.z, fabsf(v.z)), fmaxf(m.w, fabsf(v.w)));
 }
 
-// Column |x| maxima of one chunk of rows: grid.x spans the channel groups,
-// grid.y the row chunks.  The partial of chunk k for quad G (channels 4G ..
-// 4G + 3) goes to part[G * chunks + k], so the reduction reads each quad's
-// partials contiguously.
+// Column |x| maxima of one chunk of rows.  grid.x spans the channel groups,
+// kWave quads per workgroup, grid.y the row chunks; each of the workgroup's
+// waves takes one contiguous slice of the chunk's rows (more loads in flight
+// per CU than one wave per column range), and LDS joins the slices.  The
+// partial of chunk k for quad G (channels 4G .. 4G + 3) goes to
+// part[G * chunks + k], so the reduction reads each quad's partials
+// contiguously.
 template <int DT>
 __global__ __launch_bounds__(kKvThreads) void kv_amax_partial(const void* __restrict__ kv, int64_t ld, int T,
                                                               int CQ, int rows_per_chunk, int chunks,
                                                               float4* __restrict__ part) {
     constexpr int Q = kv_quads<DT>();
-    const int g = blockIdx.x * kKvThreads + threadIdx.x;  // channels [4Qg, 4Qg + 4Q)
-    if (g >= CQ) return;
+    constexpr int S = kKvThreads / kWave;  // row slices, one per wave
+    __shared__ float4 red[S - 1][Q][kWave];
+    const int lane = threadIdx.x % kWave;
+    const int w = threadIdx.x / kWave;
+    const int g = blockIdx.x * kWave + lane;  // channels [4Qg, 4Qg + 4Q)
+    const bool live = g < CQ;
     const int r0 = blockIdx.y * rows_per_chunk;
-    const int r1 = min(T, r0 + rows_per_chunk);
+    const int n = max(0, min(T - r0, rows_per_chunk));
+    const int per = (n + S - 1) / S;
+    const int r1 = r0 + min(n, (w + 1) * per);
     const int64_t e0 = 4 * Q * (int64_t)g;
     float4 m[Q];
 #pragma unroll
     for (int q = 0; q < Q; ++q) m[q] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    int r = r0;
-    for (; r + kKvUnroll <= r1; r += kKvUnroll) {
-        float4 v[kKvUnroll][Q];
+    if (live) {
+        int r = r0 + min(n, w * per);
+        for (; r + kKvUnroll <= r1; r += kKvUnroll) {
+            float4 v[kKvUnroll][Q];
 #pragma unroll
-        for (int i = 0; i < kKvUnroll; ++i) kv_load<DT>(kv, (int64_t)(r + i) * ld + e0, v[i]);
+            for (int i = 0; i < kKvUnroll; ++i) kv_load<DT>(kv, (int64_t)(r + i) * ld + e0, v[i]);
 #pragma unroll
-        for (int i = 0; i < kKvUnroll; ++i)
+            for (int i = 0; i < kKvUnroll; ++i)
 #pragma unroll
-            for (int q = 0; q < Q; ++q) m[q] = abs_max4(m[q], v[i][q]);
+                for (int q = 0; q < Q; ++q) m[q] = abs_max4(m[q], v[i][q]);
+        }
+        for (; r < r1; ++r) {
+            float4 v[Q];
+            kv_load<DT>(kv, (int64_t)r * ld + e0, v);
+#pragma unroll
+            for (int q = 0; q < Q; ++q) m[q] = abs_max4(m[q], v[q]);
+        }
     }
-    for (; r < r1; ++r) {
-        float4 v[Q];
-        kv_load<DT>(kv, (int64_t)r * ld + e0, v);
+    if (w > 0) {
 #pragma unroll
-        for (int q = 0; q < Q; ++q) m[q] = abs_max4(m[q], v[q]);
+        for (int q = 0; q < Q; ++q) red[w - 1][q][lane] = m[q];
     }
+    __syncthreads();
+    if (w == 0 && live) {
 #pragma unroll
-    for (int q = 0; q < Q; ++q) part[((int64_t)Q * g + q) * chunks + blockIdx.y] = m[q];
+        for (int k = 0; k < S - 1; ++k)
+#pragma unroll
+            for (int q = 0; q < Q; ++q) {
+                const float4 o = red[k][q][lane];
+                m[q] = make_float4(fmaxf(m[q].x, o.x), fmaxf(m[q].y, o.y), fmaxf(m[q].z, o.z), fmaxf(m[q].w, o.w));
+            }
+#pragma unroll
+        for (int q = 0; q < Q; ++q) part[((int64_t)Q * g + q) * chunks + blockIdx.y] = m[q];
+    }
 }
 
 // One wave per channel group: the 64 lanes stride over the chunks' partials,
@@ -351,7 +376,7 @@ namespace {
 // pass is fastest with one workgroup per CU, each streaming long column
 // ranges (42 us vs 54 us at 4 per CU); quantize and read back with about 8
 // per CU.
-constexpr int64_t kKvAmaxBlocks = 256;
+constexpr int64_t kKvAmaxBlocks = 1024;
 constexpr int64_t kKvTargetBlocks = 2048;
 constexpr int64_t kKvMinRows = 16;
 
@@ -370,7 +395,7 @@ int64_t rows_per_block(int64_t T, int64_t col_blocks, int64_t target) {
 // Row chunks of the channel-maxima pass for rows read `quads` channel quads
 // per thread (1 for fp32, 2 for 16-bit elements).
 KvChunks kv_amax_chunks(int64_t T, int64_t C, int quads) {
-    const int64_t col_blocks = ceil_div(C / 4 / quads, kKvThreads);
+    const int64_t col_blocks = ceil_div(C / 4 / quads, kWave);
     const int64_t rpc = rows_per_block(T, std::max<int64_t>(col_blocks, 1), kKvAmaxBlocks);
     return KvChunks{(int)rpc, (int)std::max<int64_t>(1, ceil_div(T, rpc))};
 }
@@ -394,7 +419,7 @@ hipError_t launch_kv_channel_scales(const void* kv, int dtype, int64_t T, int64_
 #define FP8K_KV_AMAX(D)                                                                                              \
     {                                                                                                                \
         const int cq = C4 / kv_quads<D>();                                                                           \
-        const dim3 g1((unsigned)ceil_div(cq, kKvThreads), (unsigned)ch.chunks);                                      \
+        const dim3 g1((unsigned)ceil_div(cq, kWave), (unsigned)ch.chunks);                                           \
         hipLaunchKernelGGL(kv_amax_partial<D>, g1, dim3(kKvThreads), 0, stream, kv, ldkv, (int)T, cq, ch.rows_per_chunk, \
                            ch.chunks, part);                                                                         \
     }

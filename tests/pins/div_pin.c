@@ -1,8 +1,9 @@
 /*
  * Check of the division method the GPU quantizer uses: for a row scale s and
- * an element x it forms r = RN(1/s), q0 = RN(x * r), e = x - q0 * s (one FMA,
- * exact) and q = RN(q0 + e * r) (one FMA), with the sign of x put back (so
- * x = -0 gives -0).  The claim checked here is q == RN(x / s) bit for bit,
+ * an element x it forms r = RN(1/s), q0 = RN(x * r), d = q0 * s - x (one FMA,
+ * exact) and q = RN(q0 - d * r) (one FMA); with the residual in that order
+ * x = -0 gives -0 (d = +0, q = -0 - 0), so no sign fix-up follows.  The claim
+ * checked here is q == RN(x / s) bit for bit,
  * except for subnormal x (see agree() below), where the E4M3 code is the
  * same signed zero either way; the reference quotient is binary64 division
  * rounded to binary32, which is correctly rounded because 53 >= 2 * 24 + 2.
@@ -34,9 +35,8 @@ static uint64_t sm64(uint64_t* st) {
 static float method(float x, float s) {
     const float r = (float)(1.0 / (double)s);
     const float q0 = fminf(fmaxf(x * r, -0x1p20f), 0x1p20f);
-    const float e = fmaf(-q0, s, x);
-    const float q1 = fmaf(e, r, q0);
-    return copysignf(q1, x);
+    const float d = fmaf(q0, s, -x);
+    return fmaf(d, -r, q0);
 }
 
 static float exact(float x, float s) { return (float)((double)x / (double)s); }

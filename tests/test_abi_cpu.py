@@ -241,7 +241,7 @@ def test_kv_validation():
     E4, E5 = fp8.FP8_KV_E4M3, fp8.FP8_KV_E5M2
     # workspace: one fp32 partial maximum per channel and row chunk (about 256 workgroups in all)
     assert L.fp8_kv_scales_workspace_bytes(32768, 2048) == 256 * 2048 * 4   # 16-bit rows: 1 column block
-    assert L.fp8_kv_scales_workspace_bytes(32768, 576) == 256 * 576 * 4
+    assert L.fp8_kv_scales_workspace_bytes(32768, 576) == 512 * 576 * 4
     assert L.fp8_kv_scales_workspace_bytes(0, 576) == 576 * 4          # one chunk; 2304 = 9 * 256
     assert L.fp8_kv_scales_workspace_bytes(0, 68) == 512              # rounded up to 256 bytes
     assert L.fp8_kv_scales_workspace_bytes(10, 6) == ctypes.c_size_t(-1).value     # C % 4
