@@ -279,16 +279,16 @@ __global__ __launch_bounds__(kKvThreads) void kv_quantize_paged(const void* __re
     const int r1 = min(T, r0 + rows_per_block);
     const int64_t e0 = 4 * Q * (int64_t)g;
     const int64_t C = 4 * Q * (int64_t)CQ;  // cache row length in bytes
-    auto put = [&](int s, const float4 (&v)[Q]) {
+    auto encode = [&](const float4 (&v)[Q], uint32_t (&w)[Q]) {
+#pragma unroll
+        for (int q = 0; q < Q; ++q) w[q] = kv_encode4<FMT>(v[q], rs[q]);
+    };
+    auto put = [&](int s, const uint32_t (&w)[Q]) {
         uint8_t* dst = cache + (int64_t)s * C + e0;
-        if constexpr (Q == 1) {
-            *reinterpret_cast<uint32_t*>(dst) = kv_encode4<FMT>(v[0], rs[0]);
-        } else {
-            v2u w;
-            w[0] = kv_encode4<FMT>(v[0], rs[0]);
-            w[1] = kv_encode4<FMT>(v[1], rs[1]);
-            *reinterpret_cast<v2u*>(dst) = w;
-        }
+        if constexpr (Q == 1)
+            *reinterpret_cast<uint32_t*>(dst) = w[0];
+        else
+            *reinterpret_cast<v2u*>(dst) = v2u{w[0], w[1]};
     };
     int r = r0;
     for (; r + U <= r1; r += U) {
@@ -299,16 +299,29 @@ __global__ __launch_bounds__(kKvThreads) void kv_quantize_paged(const void* __re
             sl[i] = slot[r + i];
             kv_load<DT>(kv, (int64_t)(r + i) * ld + e0, v[i]);
         }
+        // Every row is encoded, and only the store depends on its slot: were
+        // the encode left inside the slot test, the compiler would sink a
+        // row's load into that branch, and the wait for that load (the last
+        // one issued) would also wait for all the others.
+        uint32_t w[U][Q];
+#pragma unroll
+        for (int i = 0; i < U; ++i) {
+            encode(v[i], w[i]);
+#pragma unroll
+            for (int q = 0; q < Q; ++q) asm volatile("" : "+v"(w[i][q]));
+        }
 #pragma unroll
         for (int i = 0; i < U; ++i)
-            if (sl[i] >= 0 && sl[i] < num_slots) put(sl[i], v[i]);
+            if (sl[i] >= 0 && sl[i] < num_slots) put(sl[i], w[i]);
     }
     for (; r < r1; ++r) {
         const int s = slot[r];
         if (s >= 0 && s < num_slots) {
             float4 v[Q];
+            uint32_t w[Q];
             kv_load<DT>(kv, (int64_t)r * ld + e0, v);
-            put(s, v);
+            encode(v, w);
+            put(s, w);
         }
     }
 }
