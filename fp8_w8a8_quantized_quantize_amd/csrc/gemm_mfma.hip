@@ -38,6 +38,8 @@
 // The output tile leaves through LDS (scaled, BF16, swizzled) so that the
 // global stores are 16-byte row-contiguous; the tile's scales are staged in
 // LDS at the start.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -383,10 +385,13 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_mfma_kernel(MfmaArgs p) 
 
     const int KT = p.K / kBK;
     const int arow0 = wn * (BN / WN) + r32;
-    const int brow0 = wm * (BM / WM) + r32;
+    // Activation fragment b of wave (wn, wm) covers tile rows
+    // (b * WM + wm) * 32 .. + 31: the waves along M take alternate 32-row
+    // blocks, so a partly filled tile leaves them equal shares of real rows.
+    const int brow0 = wm * 32 + r32;
     auto read_a = [&](int slot, int h, int a) { return read_frag(smem + slot * STAGE, arow0 + a * 32, h, g); };
     auto read_b = [&](int slot, int h, int b) {
-        return read_frag(smem + slot * STAGE + BN * kBK, brow0 + b * 32, h, g);
+        return read_frag(smem + slot * STAGE + BN * kBK, brow0 + b * (32 * WM), h, g);
     };
 
     // Block scales (MX): the word of 4 exponent bytes of each of the lane's
@@ -399,7 +404,7 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_mfma_kernel(MfmaArgs p) 
 #pragma unroll
             for (int a = 0; a < FN; ++a) wa[a] = base[arow0 + a * 32];
 #pragma unroll
-            for (int b = 0; b < FM; ++b) wb[b] = base[BN + brow0 + b * 32];
+            for (int b = 0; b < FM; ++b) wb[b] = base[BN + brow0 + b * (32 * WM)];
         }
     };
     auto next_scales = [&]() {
@@ -422,91 +427,112 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_mfma_kernel(MfmaArgs p) 
     // the compiler pairs the reads into ds_read2_b32
     constexpr int SR = MX ? (FN + FM) / 2 : 0;
 
-    v8i fa[FN], fb[FM];
-    if (KT > 0) {
-        // prologue: stages 0 and 1 in flight, stage 0 landed everywhere,
-        // its first-half fragments in registers
-        issue_stage(0, 0);
-        if (KT > 1) issue_stage(1, 1);
-        wait_dma<PER_STAGE>(KT > 1 ? 1 : 0);
-        block_barrier();
-        read_scales(0, sc_a, sc_b);
+    // The K loop for FA active activation fragments per wave (FA <= FM).  A
+    // wave whose last fragments cover only rows past the tile's real rows
+    // (the last row tile of an expert) skips their MFMAs and LDS reads; its
+    // DMA share, waits and barriers are the same for every FA, so the waves
+    // of one workgroup stay in step whatever their FA.
+    auto k_loop = [&](auto fa_count) {
+        constexpr int FA = decltype(fa_count)::value;
+        v8i fa[FN], fb[FA];
+        if (KT > 0) {
+            // prologue: stages 0 and 1 in flight, stage 0 landed everywhere,
+            // its first-half fragments in registers
+            issue_stage(0, 0);
+            if (KT > 1) issue_stage(1, 1);
+            wait_dma<PER_STAGE>(KT > 1 ? 1 : 0);
+            block_barrier();
+            read_scales(0, sc_a, sc_b);
 #pragma unroll
-        for (int b = 0; b < FM; ++b) fb[b] = read_b(0, 0, b);
+            for (int b = 0; b < FA; ++b) fb[b] = read_b(0, 0, b);
 #pragma unroll
-        for (int a = 0; a < FN; ++a) fa[a] = read_a(0, 0, a);
-    }
-    // Steps with a stage s+2 to load: no branches in the body, the DMA
-    // instructions of stage s+2 issued one per second-half MFMA (in program
-    // order they must precede the LDS reads that follow them, which keeps them
-    // spread out instead of in one burst after the barrier).
-    static_assert(PER_STAGE <= 2 * FN * FM, "at most two DMA instructions per second-half MFMA");
-    int s = 0;
-    for (; s + 2 < KT; ++s) {
-        const int cur = s & 1;
-#pragma unroll
-        for (int a = 0; a < FN; ++a) {
-#pragma unroll
-            for (int b = 0; b < FM; ++b) {
-                acc[a][b] = mma(fa[a], fb[b], acc[a][b], a, b, 0);
-                if (a == FN - 1) fb[b] = read_b(cur, 1, b);
-            }
-            fa[a] = read_a(cur, 1, a);
+            for (int a = 0; a < FN; ++a) fa[a] = read_a(0, 0, a);
         }
-        interleave_mfma_reads<FN * FM, 2 * (FN + FM)>();
-        wait_dma<PER_STAGE>(0);  // this wave's part of stage s+1 landed
-        wait_lds_reads();        // ... and its reads of stage s are done
-        block_barrier();
-        read_scales(cur ^ 1, nx_a, nx_b);
+        // Steps with a stage s+2 to load: no branches in the body, the DMA
+        // instructions of stage s+2 dealt round-robin to the second-half MFMAs
+        // (in program order they must precede the LDS reads that follow them,
+        // which keeps them spread out instead of in one burst after the barrier).
+        int s = 0;
+        for (; s + 2 < KT; ++s) {
+            const int cur = s & 1;
 #pragma unroll
-        for (int a = 0; a < FN; ++a) {
+            for (int a = 0; a < FN; ++a) {
 #pragma unroll
-            for (int b = 0; b < FM; ++b) {
-                acc[a][b] = mma(fa[a], fb[b], acc[a][b], a, b, 1);
-                if (a * FM + b < PER_STAGE) issue_one(s + 2, cur, a * FM + b);
-                if (a * FM + b + FN * FM < PER_STAGE) issue_one(s + 2, cur, a * FM + b + FN * FM);
-                if (a == FN - 1) fb[b] = read_b(cur ^ 1, 0, b);
+                for (int b = 0; b < FA; ++b) {
+                    acc[a][b] = mma(fa[a], fb[b], acc[a][b], a, b, 0);
+                    if (a == FN - 1) fb[b] = read_b(cur, 1, b);
+                }
+                fa[a] = read_a(cur, 1, a);
             }
-            fa[a] = read_a(cur ^ 1, 0, a);
-        }
-        interleave_mfma_reads<FN * FM, 2 * (FN + FM) + SR>();
-        next_scales();
-    }
-    // The last two steps (nothing left to load).
-    for (; s < KT; ++s) {
-        const int cur = s & 1;
-        const bool more = s + 1 < KT;
-        // first K half of stage s; refill with the second half
-#pragma unroll
-        for (int a = 0; a < FN; ++a) {
-#pragma unroll
-            for (int b = 0; b < FM; ++b) {
-                acc[a][b] = mma(fa[a], fb[b], acc[a][b], a, b, 0);
-                if (a == FN - 1) fb[b] = read_b(cur, 1, b);
-            }
-            fa[a] = read_a(cur, 1, a);
-        }
-        interleave_mfma_reads<FN * FM, 2 * (FN + FM)>();
-        if (more) {
-            wait_dma<PER_STAGE>(0);
-            wait_lds_reads();
+            interleave_mfma_reads<FN * FA, 2 * (FN + FA)>();
+            wait_dma<PER_STAGE>(0);  // this wave's part of stage s+1 landed
+            wait_lds_reads();        // ... and its reads of stage s are done
             block_barrier();
             read_scales(cur ^ 1, nx_a, nx_b);
-        }
-        // second K half of stage s; refill with the first half of stage s+1
-        // (the last step re-reads its own slot, unused)
-        const int nxt = more ? cur ^ 1 : cur;
 #pragma unroll
-        for (int a = 0; a < FN; ++a) {
+            for (int a = 0; a < FN; ++a) {
 #pragma unroll
-            for (int b = 0; b < FM; ++b) {
-                acc[a][b] = mma(fa[a], fb[b], acc[a][b], a, b, 1);
-                if (a == FN - 1) fb[b] = read_b(nxt, 0, b);
+                for (int b = 0; b < FA; ++b) {
+                    acc[a][b] = mma(fa[a], fb[b], acc[a][b], a, b, 1);
+#pragma unroll
+                    for (int j = a * FA + b; j < PER_STAGE; j += FN * FA) issue_one(s + 2, cur, j);
+                    if (a == FN - 1) fb[b] = read_b(cur ^ 1, 0, b);
+                }
+                fa[a] = read_a(cur ^ 1, 0, a);
             }
-            fa[a] = read_a(nxt, 0, a);
+            interleave_mfma_reads<FN * FA, 2 * (FN + FA) + SR>();
+            next_scales();
         }
-        interleave_mfma_reads<FN * FM, 2 * (FN + FM)>();
-        if (more) next_scales();
+        // The last two steps (nothing left to load).
+        for (; s < KT; ++s) {
+            const int cur = s & 1;
+            const bool more = s + 1 < KT;
+            // first K half of stage s; refill with the second half
+#pragma unroll
+            for (int a = 0; a < FN; ++a) {
+#pragma unroll
+                for (int b = 0; b < FA; ++b) {
+                    acc[a][b] = mma(fa[a], fb[b], acc[a][b], a, b, 0);
+                    if (a == FN - 1) fb[b] = read_b(cur, 1, b);
+                }
+                fa[a] = read_a(cur, 1, a);
+            }
+            interleave_mfma_reads<FN * FA, 2 * (FN + FA)>();
+            if (more) {
+                wait_dma<PER_STAGE>(0);
+                wait_lds_reads();
+                block_barrier();
+                read_scales(cur ^ 1, nx_a, nx_b);
+            }
+            // second K half of stage s; refill with the first half of stage s+1
+            // (the last step re-reads its own slot, unused)
+            const int nxt = more ? cur ^ 1 : cur;
+#pragma unroll
+            for (int a = 0; a < FN; ++a) {
+#pragma unroll
+                for (int b = 0; b < FA; ++b) {
+                    acc[a][b] = mma(fa[a], fb[b], acc[a][b], a, b, 1);
+                    if (a == FN - 1) fb[b] = read_b(nxt, 0, b);
+                }
+                fa[a] = read_a(nxt, 0, a);
+            }
+            interleave_mfma_reads<FN * FA, 2 * (FN + FA)>();
+            if (more) next_scales();
+        }
+    };
+    // Fragments holding at least one real row (at least 1, so that every wave
+    // runs the loop body; a wave with none computes one discarded fragment).
+    const int fa_live = min(FM, max(1, (rows_valid - wm * 32 + 32 * WM - 1) / (32 * WM)));
+    if constexpr (GROUPED && FM == 4) {
+        switch (fa_live) {
+            case 1: k_loop(std::integral_constant<int, 1>{}); break;
+            case 2: k_loop(std::integral_constant<int, 2>{}); break;
+            case 3: k_loop(std::integral_constant<int, 3>{}); break;
+            default: k_loop(std::integral_constant<int, 4>{}); break;
+        }
+    } else {
+        (void)fa_live;
+        k_loop(std::integral_constant<int, FM>{});
     }
 
     // ---- epilogue: y = bf16_rne(acc * (s_tok * s_ch)) ----------------------
@@ -522,7 +548,7 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_mfma_kernel(MfmaArgs p) 
             const bool vec = (p.ldy & 3) == 0;
 #pragma unroll
             for (int b = 0; b < FM; ++b) {
-                const int ml = wm * (BM / WM) + b * 32 + r32;
+                const int ml = (b * WM + wm) * 32 + r32;
                 if (ml >= rows_valid) continue;
                 const float st = s_tok_t[ml];
                 float* yr = p.y32 + (int64_t)(m0 + ml) * p.ldy;
@@ -556,7 +582,7 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_mfma_kernel(MfmaArgs p) 
     constexpr int CH = BN / 8;  // 16-byte chunks per tile row
 #pragma unroll
     for (int b = 0; b < FM; ++b) {
-        const int ml = wm * (BM / WM) + b * 32 + r32;
+        const int ml = (b * WM + wm) * 32 + r32;
         const float st = s_tok_t[ml];
 #pragma unroll
         for (int a = 0; a < FN; ++a) {
@@ -649,8 +675,8 @@ hipError_t launch_gemm_grouped_mfma(const uint8_t* qa, const float* s_tok, const
     constexpr int GM = 4;
     hipError_t e = FP8K_SET_LDS((gemm_mfma_kernel<BN, BM, WN, WM, GM, true>), LDS);
     if (e != hipSuccess) return e;
-    // sum over experts of ceil(rows_e / BM) <= ceil(R / BM) + E; each of the 8
-    // XCD ranges holds at most ceil(total / 8) tiles
+    // sum over experts of ceil(rows_e / BM) <= ceil(R / BM) + E tiles; each
+    // XCD holds at most ceil(hot / 8) + ceil(cold / 8) <= ceil(tiles / 8) + 1
     const int64_t tiles_max = ((R + BM - 1) / BM + E) * p.tiles_n;
     const int64_t grid = 8 * ((tiles_max + 7) / 8);
     hipLaunchKernelGGL((gemm_mfma_kernel<BN, BM, WN, WM, GM, true>), dim3((unsigned)grid), dim3(64 * WN * WM), LDS, stream,

@@ -269,6 +269,30 @@ def test_grouped_with_empty_experts():
     assert_within_tolerance(y.reshape(-1), ref, ab, "grouped empty experts")
 
 
+def test_grouped_partial_row_tiles():
+    """Expert loads at and around every 32-row boundary of a 256-row tile:
+    the last row tile of an expert computes only the 32-row activation
+    fragments that hold real rows, dealt alternately to the two waves along
+    M, so each count of live fragments (1 to 4 per wave, both waves) occurs."""
+    T, N, K = 700, 512, 256
+    loads = np.array([1, 31, 32, 33, 63, 64, 65, 95, 96, 97, 127, 128, 129, 159, 160, 161, 191, 192, 193,
+                      223, 224, 225, 255, 256, 257, 300, 511, 512, 513], np.int32)
+    log(f"grouped partial tiles: {loads.size} experts, R={int(loads.sum())} N={N} K={K}")
+    rng = np.random.default_rng(11)
+    off = np.concatenate([[0], np.cumsum(loads)]).astype(np.int32)
+    R = int(off[-1])
+    rt = rng.integers(0, T, R).astype(np.int32)
+    E = loads.size
+    qa = rng.choice(FINITE, (T, K)).astype(np.uint8)
+    st = rng.uniform(0.01, 1, T).astype(np.float32)
+    qw = rng.choice(FINITE, (E, N, K)).astype(np.uint8)
+    sc = rng.uniform(0.01, 1, (E, N)).astype(np.float32)
+    y = _grouped(qa, st, rt, off, qw, sc)
+    rs, ns = np.repeat(np.arange(R), N), np.tile(np.arange(N), R)
+    ref, ab = oracle.grouped_ref_sampled(qa, st, rt, off, qw, sc, rs, ns)
+    assert_within_tolerance(y.reshape(-1), ref, ab, "grouped partial row tiles")
+
+
 def test_grouped_moe_workload():
     w = synth.WORKLOADS["moe-64x2048x7168"]
     T, E, k, N, K = w["T"], w["E"], w["topk"], w["N"], w["K"]
