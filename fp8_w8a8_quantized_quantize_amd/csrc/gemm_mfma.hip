@@ -230,6 +230,13 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_mfma_kernel(MfmaArgs p) 
     static_assert(!MX || DS * 64 * NW == BN + BM, "whole scale DMA instructions per wave");
     static_assert(BM * BN * 2 <= 2 * STAGE, "the BF16 output tile must fit in the ring");
     int* sh = reinterpret_cast<int*>(smem + 2 * STAGE + 4 * (BN + BM));  // grouped tile lookup
+    // Grouped: the weight tile's lines of stage s + 3 are touched into L2
+    // during step s (one 4-byte DMA per row into a dummy LDS slot), so the
+    // stage's own DMA one step later finds them there: expert weights stream
+    // from HBM, whose latency one step of MFMAs does not always cover.
+    constexpr bool PF = GROUPED;
+    static_assert(!PF || BN == 64 * NW, "one prefetch row per lane");
+    uint8_t* pf_lds = smem + 2 * STAGE + 4 * (BN + BM) + 16;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -324,6 +331,10 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_mfma_kernel(MfmaArgs p) 
         bsrc[j] = p.qa + src_row * lda + ((lpos ^ dswz(row)) << 4);
     }
     const int nlast = p.N - 1;
+    const uint8_t* pf_src = qw + (int64_t)min(n0 + wave * 64 + lane, nlast) * ldw;
+    auto prefetch_a = [&](int kt) {
+        if constexpr (PF) __builtin_amdgcn_global_load_lds(pf_src + kt * kBK, pf_lds, 4, 0, 0);
+    };
     // Block-scale DMA (MX): instruction j of this wave fetches the stage's
     // scale words of tile rows (wave * DS + j) * 64 + lane, weight rows first.
     const uint8_t* ssrc[DS + 1];
@@ -440,7 +451,15 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_mfma_kernel(MfmaArgs p) 
             // its first-half fragments in registers
             issue_stage(0, 0);
             if (KT > 1) issue_stage(1, 1);
-            wait_dma<PER_STAGE>(KT > 1 ? 1 : 0);
+            if (PF && KT > 2) prefetch_a(2);
+            if (PF && KT > 2) {
+                static_assert(PER_STAGE + 1 <= 63, "vmcnt field");
+                compiler_fence();
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PER_STAGE + 1) : "memory");
+                compiler_fence();
+            } else {
+                wait_dma<PER_STAGE>(KT > 1 ? 1 : 0);
+            }
             block_barrier();
             read_scales(0, sc_a, sc_b);
 #pragma unroll
@@ -465,7 +484,15 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_mfma_kernel(MfmaArgs p) 
                 fa[a] = read_a(cur, 1, a);
             }
             interleave_mfma_reads<FN * FA, 2 * (FN + FA)>();
-            wait_dma<PER_STAGE>(0);  // this wave's part of stage s+1 landed
+            // this wave's part of stage s+1 landed (with prefetching, the
+            // touch of stage s+2, issued after it, may still be in flight)
+            if constexpr (PF) {
+                compiler_fence();
+                asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
+                compiler_fence();
+            } else {
+                wait_dma<PER_STAGE>(0);
+            }
             wait_lds_reads();        // ... and its reads of stage s are done
             block_barrier();
             read_scales(cur ^ 1, nx_a, nx_b);
@@ -481,6 +508,7 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_mfma_kernel(MfmaArgs p) 
                 fa[a] = read_a(cur ^ 1, 0, a);
             }
             interleave_mfma_reads<FN * FA, 2 * (FN + FA) + SR>();
+            if (PF && s + 3 < KT) prefetch_a(s + 3);  // issued last: the next step waits for all but it
             next_scales();
         }
         // The last two steps (nothing left to load).
@@ -666,7 +694,7 @@ hipError_t launch_gemm_grouped_mfma(const uint8_t* qa, const float* s_tok, const
     (void)T;
     if (R <= 0 || N <= 0 || E <= 0) return hipSuccess;
     constexpr int BN = 256, BM = 256, WN = 2, WM = 2;
-    constexpr int LDS = 2 * (BN + BM) * kBK + 4 * (BN + BM) + 16;  // ring + tile scales + tile lookup
+    constexpr int LDS = 2 * (BN + BM) * kBK + 4 * (BN + BM) + 16 + 256;  // ring + tile scales + tile lookup + prefetch slot
     MfmaArgs p{};
     p.qa = qa; p.lda = K; p.s_tok = s_tok; p.qw = qw; p.ldw = K; p.s_ch = s_ch; p.y = y; p.ldy = N;
     p.M = (int)R; p.N = (int)N; p.K = (int)K;
