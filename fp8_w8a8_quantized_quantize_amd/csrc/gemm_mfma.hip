@@ -5,7 +5,8 @@
 //
 // Tile: BN weight rows (MFMA A operand) x BM activation rows (MFMA B operand),
 // 128 bytes of K per stage, two stages in LDS.  WN x WM waves, each owning
-// (BN/WN) x (BM/WM) outputs as 32x32x64 FP8 MFMA tiles (16 accumulators per
+// BN/WN weight rows times every WM-th 32-row block of activation rows
+// ((BN/WN) x (BM/WM) outputs) as 32x32x64 FP8 MFMA tiles (16 accumulators per
 // lane per tile); a stage is consumed as two 64-wide K halves.  The launchers
 // use 2 x 2 waves of 128 x 128: measured on MI355X, 2 x 4 waves (two per SIMD,
 // which doubles the LDS read rate a CU reaches) lose more to the 50% larger
@@ -703,8 +704,8 @@ hipError_t launch_gemm_grouped_mfma(const uint8_t* qa, const float* s_tok, const
     constexpr int GM = 4;
     hipError_t e = FP8K_SET_LDS((gemm_mfma_kernel<BN, BM, WN, WM, GM, true>), LDS);
     if (e != hipSuccess) return e;
-    // sum over experts of ceil(rows_e / BM) <= ceil(R / BM) + E tiles; each
-    // XCD holds at most ceil(hot / 8) + ceil(cold / 8) <= ceil(tiles / 8) + 1
+    // sum over experts of ceil(rows_e / BM) <= ceil(R / BM) + E; each of the 8
+    // XCD ranges holds at most ceil(total / 8) tiles
     const int64_t tiles_max = ((R + BM - 1) / BM + E) * p.tiles_n;
     const int64_t grid = 8 * ((tiles_max + 7) / 8);
     hipLaunchKernelGGL((gemm_mfma_kernel<BN, BM, WN, WM, GM, true>), dim3((unsigned)grid), dim3(64 * WN * WM), LDS, stream,
