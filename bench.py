@@ -71,7 +71,8 @@ def parse():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run 5 plain device copies of 512 MiB (reference for rocprofv3 FETCH/WRITE_SIZE)")
     ap.add_argument("--profile", action="store_true",
-                    help="few steps, no CPU baseline: for runs under rocprofv3")
+                    help="at most 50 timed steps after the usual warm-up, no CPU baseline: for runs under "
+                         "rocprofv3 (the GPU clock needs the warm-up to settle)")
     return ap.parse_args()
 
 
@@ -210,7 +211,7 @@ def main():
     w = synth.WORKLOADS[args.workload]
     steps, warmup = args.steps, args.warmup
     if args.profile:
-        steps, warmup = min(steps, 10), min(warmup, 3)
+        steps = min(steps, 50)
     log = lambda *a: print(*a, file=sys.stderr, flush=True)
     graph = not args.no_graph
 
