@@ -269,12 +269,15 @@ def test_grouped_with_empty_experts():
     assert_within_tolerance(y.reshape(-1), ref, ab, "grouped empty experts")
 
 
-def test_grouped_partial_row_tiles():
+@pytest.mark.parametrize("K", [128, 256, 384, 640])
+def test_grouped_partial_row_tiles(K):
     """Expert loads at and around every 32-row boundary of a 256-row tile:
     the last row tile of an expert computes only the 32-row activation
     fragments that hold real rows, dealt alternately to the two waves along
-    M, so each count of live fragments (1 to 4 per wave, both waves) occurs."""
-    T, N, K = 700, 512, 256
+    M, so each count of live fragments (1 to 4 per wave, both waves) occurs.
+    K of 1, 2, 3 and 5 stages of 128 covers each way the weight lines of a
+    later stage are touched ahead (none, in the prologue, in the loop)."""
+    T, N = 700, 512
     loads = np.array([1, 31, 32, 33, 63, 64, 65, 95, 96, 97, 127, 128, 129, 159, 160, 161, 191, 192, 193,
                       223, 224, 225, 255, 256, 257, 300, 511, 512, 513], np.int32)
     log(f"grouped partial tiles: {loads.size} experts, R={int(loads.sum())} N={N} K={K}")
