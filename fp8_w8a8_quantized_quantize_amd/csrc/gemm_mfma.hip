@@ -214,7 +214,11 @@ __device__ void find_expert_tile(const MfmaArgs& p, int b, int* sh) {
 // consecutive rows are contiguous: a row-major [row][kt] order made every
 // lane of a scale DMA touch its own cache line (measured: 23 % slower on
 // 8192^3).
-template <int BN, int BM, int WN, int WM, int GROUP_M, bool GROUPED, bool MX = false>
+// SKIP (dense): compile the K loop for 1-4 live activation fragments, as the
+// grouped kernel always does; the launcher takes it only when the whole grid
+// is one row of tiles with at most 192 real rows (M in 65..192), because the
+// extra instantiations cost the full-tile loop about 1 % (measured on 8192^3).
+template <int BN, int BM, int WN, int WM, int GROUP_M, bool GROUPED, bool MX = false, bool SKIP = false>
 __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_mfma_kernel(MfmaArgs p) {
     static_assert(!(MX && GROUPED), "block scales: dense GEMM only");
     constexpr int NW = WN * WM;                 // waves: WN along the weight rows, WM along the activations
@@ -441,7 +445,7 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_mfma_kernel(MfmaArgs p) 
 
     // The K loop for FA active activation fragments per wave (FA <= FM).  A
     // wave whose last fragments cover only rows past the tile's real rows
-    // (the last row tile of an expert) skips their MFMAs and LDS reads; its
+    // (the last row tile of an expert, or of a short M) skips their MFMAs and LDS reads; its
     // DMA share, waits and barriers are the same for every FA, so the waves
     // of one workgroup stay in step whatever their FA.
     auto k_loop = [&](auto fa_count) {
@@ -552,7 +556,7 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_mfma_kernel(MfmaArgs p) 
     // Fragments holding at least one real row (at least 1, so that every wave
     // runs the loop body; a wave with none computes one discarded fragment).
     const int fa_live = min(FM, max(1, (rows_valid - wm * 32 + 32 * WM - 1) / (32 * WM)));
-    if constexpr (GROUPED && FM == 4) {
+    if constexpr ((GROUPED || SKIP) && FM == 4 && !MX) {
         switch (fa_live) {
             case 1: k_loop(std::integral_constant<int, 1>{}); break;
             case 2: k_loop(std::integral_constant<int, 2>{}); break;
@@ -662,9 +666,17 @@ hipError_t launch_gemm_mfma(const uint8_t* qa, int64_t lda, const float* s_tok, 
     p.M = (int)M; p.N = (int)N; p.K = (int)K;
     p.tiles_m = (int)((M + BM - 1) / BM);
     p.tiles_n = (int)((N + BN - 1) / BN);
+    const unsigned grid = (unsigned)p.tiles_m * (unsigned)p.tiles_n;
+    if (M <= BM - 64) {
+        // one row of tiles whose last 32-row fragments are empty for both waves along M
+        hipError_t e = FP8K_SET_LDS((gemm_mfma_kernel<BN, BM, WN, WM, 4, false, false, true>), LDS);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((gemm_mfma_kernel<BN, BM, WN, WM, 4, false, false, true>), dim3(grid), dim3(64 * WN * WM), LDS,
+                           stream, p);
+        return hipGetLastError();
+    }
     hipError_t e = FP8K_SET_LDS((gemm_mfma_kernel<BN, BM, WN, WM, 4, false>), LDS);
     if (e != hipSuccess) return e;
-    const unsigned grid = (unsigned)p.tiles_m * (unsigned)p.tiles_n;
     hipLaunchKernelGGL((gemm_mfma_kernel<BN, BM, WN, WM, 4, false>), dim3(grid), dim3(64 * WN * WM), LDS, stream, p);
     return hipGetLastError();
 }

@@ -40,7 +40,9 @@ def _gemm(qa, st, qw, sc):
 SHAPES = [(1, 16, 16), (8, 200, 160), (16, 4096 + 48, 512), (33, 300, 1040), (64, 520, 2064),
           (64, 1024, 4096), (40, 1000, 8240), (17, 300, 16384),
           (65, 272, 384), (200, 700, 1168), (513, 257, 2064), (300, 1024, 4096),
-          (129, 1000, 640), (777, 264, 1280), (256, 256, 128)]
+          (129, 1000, 640), (777, 264, 1280), (256, 256, 128),
+          # one row of MFMA tiles with empty 32-row fragments (M <= 192) and just past it
+          (96, 520, 1024), (192, 264, 256), (193, 264, 256)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
