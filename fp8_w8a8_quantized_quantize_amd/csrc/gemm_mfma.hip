@@ -646,7 +646,7 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_mfma_kernel(MfmaArgs p) 
         const int64_t yrow = GROUPED ? (int64_t)row_begin + m0 + row : (int64_t)m0 + row;
         uint16_t* dst = p.y + yrow * ldy + n;
         if (vec_store && n + 8 <= p.N) {
-            *reinterpret_cast<v4i*>(dst) = val;
+            __builtin_nontemporal_store(val, reinterpret_cast<v4i*>(dst));  // written once, read by the next layer
         } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e)
