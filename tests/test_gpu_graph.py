@@ -93,6 +93,28 @@ def test_kv_codec_graph_replays_match_eager():
     _replay_check(step, [scales, cache, out], "kv codec")
 
 
+def test_grouped_moe_step_graph_replays_match_eager():
+    """Per-token quantization + grouped GEMM (experts with partly filled and
+    several row tiles, so both the skipped fragments and the weight touch run)."""
+    T, E, N, K = 600, 6, 512, 1024
+    loads = np.array([300, 1, 95, 513, 0, 191], np.int32)
+    rng = np.random.default_rng(37)
+    off = to_dev(np.concatenate([[0], np.cumsum(loads)]).astype(np.int32))
+    rt = to_dev(rng.integers(0, T, int(loads.sum())).astype(np.int32))
+    x = to_dev(synth.activations(T, K, 10, 50.0, seed=37)[0])
+    qw, sc = fp8.fp8_quantize_per_token(to_dev(synth.weights(E * N, K, seed=37)))
+    qw, sc = qw.view(E, N, K), sc.view(E, N)
+    qa = torch.empty((T, K), dtype=torch.uint8, device=DEV)
+    st = torch.empty(T, dtype=torch.float32, device=DEV)
+    y = torch.empty((int(loads.sum()), N), dtype=torch.bfloat16, device=DEV)
+
+    def step():
+        fp8.fp8_quantize_per_token(x, q=qa, scales=st)
+        fp8.fp8_gemm_grouped_scaled(qa, st, rt, off, qw, sc, y=y)
+
+    _replay_check(step, [qa, st, y], "grouped moe step")
+
+
 @pytest.mark.parametrize("M,N,K", [(8, 4096, 1024), (64, 8192, 28672), (300, 1024, 1024)])
 def test_mx_step_graph_replays_match_eager(M, N, K):
     x = to_dev(synth.activations(M, K, max(1, synth.n_outlier_channels(K)), 50.0, seed=33)[0])
