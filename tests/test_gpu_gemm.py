@@ -242,7 +242,8 @@ def _grouped(qa, st, rt, off, qw, sc):
     return to_host(y)
 
 
-@pytest.mark.parametrize("T,E,topk,N,K", [(40, 6, 2, 272, 160), (300, 8, 3, 256, 1024), (129, 3, 1, 520, 2064)])
+@pytest.mark.parametrize("T,E,topk,N,K", [(40, 6, 2, 272, 160), (300, 8, 3, 256, 1024), (129, 3, 1, 520, 2064),
+                                           (257, 70, 4, 520, 1152)])
 def test_grouped_full_compare(T, E, topk, N, K):
     log(f"grouped T={T} E={E} topk={topk} N={N} K={K}")
     rt, off, qa, st, qw, sc = _grouped_problem(T, E, topk, N, K, seed=T)
