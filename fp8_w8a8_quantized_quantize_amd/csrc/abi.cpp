@@ -154,6 +154,11 @@ size_t fp8_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     return fused_stage_bytes(M, K) + gemm_ws_bytes(M, N, K);
 }
 
+size_t fp8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (check_dims(M, N, K) == FP8_ERR_INVALID_ARGUMENT) return SIZE_MAX;
+    return gemm_ws_bytes(M, N, K);
+}
+
 size_t fp8_fp8out_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     if (check_dims(M, N, K) == FP8_ERR_INVALID_ARGUMENT) return SIZE_MAX;
     int64_t mn;

@@ -134,7 +134,7 @@ size_t fp8_calibrate_workspace_bytes(void);
  *   y[m,n] = bf16_rne( (sum_k e4m3(qa[m,k]) * e4m3(qw[n,k])) * (s_tok[m] * s_ch[n]) )
  * Skinny M (decode, M <= 64) streams W once from HBM; larger M runs the
  * LDS-tiled MFMA kernel.  ws: device scratch of at least
- * fp8_workspace_bytes(M, N, K) bytes (may be NULL when that is 0).  Skinny
+ * fp8_gemm_workspace_bytes(M, N, K) bytes (may be NULL when that is 0).  Skinny
  * shapes with more than 16 rows, few weight rows and long K split K across
  * workgroups and keep fp32 partial sums there (added in a fixed order, so
  * results are reproducible).
@@ -212,9 +212,17 @@ fp8_status_t fp8_gemm_grouped_scaled(const uint8_t* qa, const float* s_tok,
  * invalid sizes). */
 size_t fp8_fp8out_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
-/* Workspace bytes fp8_gemm_scaled and fp8_quant_gemm_fused need for this
- * shape (host-only, pure; 0 when none is needed; SIZE_MAX for invalid sizes). */
+/* Workspace bytes fp8_quant_gemm_fused needs for this shape: the staged
+ * activation codes and scales (M * K + 4 * M bytes, each rounded up to 256)
+ * plus what the GEMM needs (host-only, pure; SIZE_MAX for invalid sizes).
+ * The one-kernel fused path touches none of it, but callers size ws with
+ * this value whatever path the shape takes. */
 size_t fp8_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/* Workspace bytes fp8_gemm_scaled needs for this shape: the skinny kernel's
+ * fp32 split-K partial sums when the shape splits K, else 0 (host-only,
+ * pure; SIZE_MAX for invalid sizes). */
+size_t fp8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* Workspace bytes fp8_gemm_grouped_scaled needs (host-only, pure). */
 size_t fp8_grouped_workspace_bytes(int64_t T, int64_t R, int64_t E, int64_t N, int64_t K);

@@ -77,6 +77,10 @@ def lib():
         L.oracle_bf16_from_double.argtypes = [f64]
         L.oracle_bf16_from_double_array.restype = None
         L.oracle_bf16_from_double_array.argtypes = [vp, i64, vp]
+        L.oracle_fp16_from_double.restype = ctypes.c_uint16
+        L.oracle_fp16_from_double.argtypes = [f64]
+        L.oracle_fp16_from_double_array.restype = None
+        L.oracle_fp16_from_double_array.argtypes = [vp, i64, vp]
         L.oracle_num_threads.restype = ctypes.c_int
         L.oracle_num_threads.argtypes = []
         L.oracle_set_num_threads.restype = None
@@ -325,6 +329,15 @@ def bf16_from_double(v):
     v = _c(v, np.float64)
     out = np.empty(v.shape, dtype=np.uint16)
     lib().oracle_bf16_from_double_array(_p(v), v.size, _p(out))
+    return out
+
+
+def fp16_from_double(v):
+    """Nearest IEEE binary16 of each double, ties to even, as uint16 bits
+    (the rounding of the 16-bit KV read back)."""
+    v = _c(v, np.float64)
+    out = np.empty(v.shape, dtype=np.uint16)
+    lib().oracle_fp16_from_double_array(_p(v), v.size, _p(out))
     return out
 
 

@@ -451,6 +451,37 @@ void oracle_bf16_from_double_array(const double* v, int64_t n, uint16_t* out) {
     for (int64_t i = 0; i < n; ++i) out[i] = oracle_bf16_from_double(v[i]);
 }
 
+/* Nearest IEEE binary16 (1-5-10 format, exponent bias 15) of a double, ties
+ * to even, as bits: the 16-bit read back of the KV cache ([SP512K] §3.3: the
+ * cache holds FP8 in place of FP16 KV).  Normal values in [2^e, 2^(e+1)),
+ * e in [-14, 15], have 10 fraction bits; below 2^-14 the grid step is 2^-24
+ * (subnormals); a value that rounds to 2^16 or beyond (|v| >= 65520) is
+ * infinite; NaN keeps its sign with the quiet bit set. */
+uint16_t oracle_fp16_from_double(double v) {
+    uint16_t sign = signbit(v) ? 0x8000 : 0;
+    if (isnan(v)) return (uint16_t)(sign | 0x7E00);
+    double a = fabs(v);
+    if (a == 0.0) return sign;
+    if (isinf(a)) return (uint16_t)(sign | 0x7C00);
+    int e2;
+    frexp(a, &e2);
+    int ex = e2 - 1;                          /* a in [2^ex, 2^(ex+1)) */
+    if (ex < -14) {
+        /* subnormal range: integer multiples of 2^-24, codes 0 .. 0x400
+           (0x400 * 2^-24 = 2^-14 is the smallest normal, exponent field 1) */
+        double r = round_half_even(ldexp(a, 24));
+        return (uint16_t)(sign | (uint16_t)r);
+    }
+    double r = round_half_even(ldexp(a, 10 - ex)); /* significand in [1024, 2048] */
+    if (r == 2048.0) { ex += 1; r = 1024.0; }
+    if (ex > 15) return (uint16_t)(sign | 0x7C00);
+    return (uint16_t)(sign | ((ex + 15) << 10) | ((int)r - 1024));
+}
+
+void oracle_fp16_from_double_array(const double* v, int64_t n, uint16_t* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_fp16_from_double(v[i]);
+}
+
 int oracle_num_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();

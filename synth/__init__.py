@@ -142,6 +142,13 @@ WORKLOADS = {
                                      desc="Llama-3-70B gate/up decode M=64 K=8192 N=28672"),
     "llama3-70b-decode-down": dict(kind="dense", M=64, K=28672, N=8192, n_out=None, mult=50.0,
                                    desc="Llama-3-70B down decode M=64 K=28672 N=8192"),
+    # one GPU's shard of the 70B decode layer at tensor-parallel degree 4 (the
+    # FFN split along the intermediate size): gate/up column-parallel (N / 4),
+    # down row-parallel (K / 4)
+    "llama3-70b-tp4-gateup": dict(kind="dense", M=64, K=8192, N=7168, n_out=None, mult=50.0,
+                                  desc="Llama-3-70B gate/up decode, TP=4 shard, M=64 K=8192 N=7168"),
+    "llama3-70b-tp4-down": dict(kind="dense", M=64, K=7168, N=8192, n_out=None, mult=50.0,
+                                desc="Llama-3-70B down decode, TP=4 shard, M=64 K=7168 N=8192"),
     "llama3-70b-prefill": dict(kind="dense", M=8192, K=8192, N=8192, n_out=None, mult=50.0,
                                desc="Llama-3-70B prefill square GEMM M=N=K=8192 with fused quantize"),
     "moe-64x2048x7168": dict(kind="moe", T=4096, E=64, topk=8, zipf=1.1, K=7168, N=2048, n_out=None,

@@ -88,3 +88,47 @@ def read_quant_examples():
                 ex.append((row, sc, codes))
                 cur = {}
     return ex
+
+
+def _code_key(c):
+    """Order of E4M3 codes by value (-0 and +0 share 0): magnitude bits,
+    negated for the sign bit."""
+    c = np.asarray(c, dtype=np.int64)
+    return np.where(c & 0x80, -(c & 0x7F), c & 0x7F)
+
+
+def fp8out_admissible(q, s, ref, absref, rel_abs=1e-3, rel_ref=2.0 ** -22):
+    """Which FP8-output codes and scales are consistent with *some* fp32
+    output y32 within the GEMM bound b = rel_abs * absref + rel_ref * |ref|
+    of the exact scaled product ref (the output the FP32 accumulation may
+    produce in any order), quantized per row as the pages define it
+    (s = max(fl32(max|y32| / 448), 1e-12f), codes E4M3(fl32(y32 / s))).
+
+    Returns dict(scale_ok [M] bool: s within [S(lo), S(hi)] where lo / hi
+    bound the row maximum of |y32|; scale_ambiguous [M]: S(lo) != S(hi);
+    code_ok [M,N]: q between the codes of the lowest and highest quotient
+    (ref -+ b) / s can take; code_ambiguous [M,N]: those two codes differ,
+    i.e. the interval holds an E4M3 rounding boundary)."""
+    import oracle
+    ref = np.asarray(ref, np.float64)
+    b = rel_abs * np.asarray(absref, np.float64) + rel_ref * np.abs(ref)
+    s = np.asarray(s, np.float32)
+    lo = np.maximum(np.abs(ref) - b, 0.0).max(axis=1) if ref.shape[1] else np.zeros(ref.shape[0])
+    hi = (np.abs(ref) + b).max(axis=1) if ref.shape[1] else np.zeros(ref.shape[0])
+    lo32 = np.nextafter(lo.astype(np.float32), np.float32(0))      # <= lo
+    hi32 = np.nextafter(hi.astype(np.float32), np.float32(np.inf))  # >= hi
+    floor = np.float32(1e-12)
+    s_lo = np.maximum(lo32 / np.float32(448.0), floor)
+    s_hi = np.maximum(hi32 / np.float32(448.0), floor)
+    scale_ok = (s >= s_lo) & (s <= s_hi)
+    sd = s.astype(np.float64)[:, None]
+    eps = 2.0 ** -23   # the quotient's own fp32 rounding, widened
+    z_lo = (ref - b) / sd
+    z_hi = (ref + b) / sd
+    z_lo = z_lo - np.abs(z_lo) * eps
+    z_hi = z_hi + np.abs(z_hi) * eps
+    c_lo = oracle.encode(np.nextafter(z_lo.astype(np.float32), np.float32(-np.inf)))
+    c_hi = oracle.encode(np.nextafter(z_hi.astype(np.float32), np.float32(np.inf)))
+    k, k_lo, k_hi = _code_key(q), _code_key(c_lo), _code_key(c_hi)
+    return dict(scale_ok=scale_ok, scale_ambiguous=s_lo != s_hi,
+                code_ok=(k >= k_lo) & (k <= k_hi), code_ambiguous=k_lo != k_hi)

@@ -333,3 +333,126 @@ def test_python_bindings_reject_host_tensors_and_bad_arguments(call):
             fp8.fp8_kv_dequantize_paged(u8, torch.zeros(4, dtype=torch.int32), torch.ones(128), "e5m2")
         else:
             fp8._kv_fmt("e4m2")
+
+
+def test_gemm_workspace_bytes_is_the_gemm_alone():
+    """fp8_gemm_workspace_bytes counts only the GEMM's split-K partial sums;
+    fp8_workspace_bytes (the fused call) adds the staged codes and scales."""
+    assert fp8.fp8_gemm_workspace_bytes(64, 8192, 28672) == 4 * 64 * 8192 * 4
+    assert fp8.fp8_gemm_workspace_bytes(8, 14336, 4096) == 0
+    assert fp8.fp8_gemm_workspace_bytes(8192, 8192, 8192) == 0
+    assert fp8.fp8_gemm_workspace_bytes(-1, 5, 16) == ctypes.c_size_t(-1).value
+    for M, N, K in [(64, 8192, 28672), (8, 14336, 4096), (8192, 8192, 8192), (300, 1024, 4096)]:
+        stage = -(-M * K // 256) * 256 + -(-4 * M // 256) * 256
+        assert fp8.fp8_workspace_bytes(M, N, K) == stage + fp8.fp8_gemm_workspace_bytes(M, N, K)
+    # a workspace of exactly the GEMM's size is accepted (qa, lda, s_tok, qw, ldw, s_ch, y, ldy, M, N, K, ws, bytes)
+    need = fp8.fp8_gemm_workspace_bytes(64, 8192, 28672)
+    assert fp8.lib().fp8_gemm_scaled(P, 28672, P, Q, 28672, P, P, 8192, 64, 8192, 28672, P, need - 1, S0) \
+        == FP8_ERR_WORKSPACE
+
+
+class _GuardLib:
+    """Stands in for the library: size queries and status names go to the real
+    one, any other entry point raises (it must never be reached here)."""
+
+    def __init__(self, real):
+        self.real = real
+
+    def __getattr__(self, name):
+        if name.endswith("_bytes") or name == "fp8_status_string":
+            return getattr(self.real, name)
+        raise AssertionError(f"{name} reached the library")
+
+
+def _stub_cls():
+    import torch
+
+    class DeviceStub(torch.Tensor):
+        """A host tensor that reports itself as a cuda:0 tensor (no GPU here), so
+        that one host tensor among them is the only thing a binding can reject."""
+
+        @property
+        def is_cuda(self):
+            return True
+
+        @property
+        def device(self):
+            return torch.device("cuda", 0)
+
+    return DeviceStub
+
+
+def _binding_case(call, host):
+    """Run binding `call` with every tensor a device stub except the one named
+    `host` (None: all stubs)."""
+    import torch
+    D = _stub_cls()
+
+    def t(name, *shape, dtype=torch.float32):
+        x = torch.zeros(*shape, dtype=dtype)
+        return x if name == host else x.as_subclass(D)
+
+    u8, f32, i32, bf = torch.uint8, torch.float32, torch.int32, torch.bfloat16
+    M, N, K = 8, 32, 128
+    ws = t("ws", 1 << 16, dtype=u8)
+    if call == "fused":
+        fp8.fp8_quant_gemm_fused(t("x", M, K), t("qw", N, K, dtype=u8), t("s_ch", N), y=t("y", M, N, dtype=bf),
+                                 qa_out=t("qa_out", M, K, dtype=u8), s_tok_out=t("s_tok_out", M), ws=ws)
+    elif call == "gemm":
+        fp8.fp8_gemm_scaled(t("qa", M, K, dtype=u8), t("s_tok", M), t("qw", N, K, dtype=u8), t("s_ch", N),
+                            y=t("y", M, N, dtype=bf), ws=ws)
+    elif call == "fp8out":
+        fp8.fp8_gemm_scaled_fp8out(t("qa", M, K, dtype=u8), t("s_tok", M), t("qw", N, K, dtype=u8), t("s_ch", N),
+                                   q_out=t("q_out", M, N, dtype=u8), s_out=t("s_out", M),
+                                   y32_out=t("y32_out", M, N), ws=ws)
+    elif call == "grouped":
+        E, T, R = 2, 4, 8
+        fp8.fp8_gemm_grouped_scaled(t("qa", T, K, dtype=u8), t("s_tok", T), t("row_token", R, dtype=i32),
+                                    t("expert_offsets", E + 1, dtype=i32), t("qw", E, N, K, dtype=u8),
+                                    t("s_ch", E, N), y=t("y", R, N, dtype=bf), ws=ws)
+    elif call == "quantize":
+        fp8.fp8_quantize_per_token(t("x", M, K), q=t("q", M, K, dtype=u8), scales=t("scales", M))
+    elif call == "gemm_mx":
+        fp8.fp8_gemm_mx(t("qa", M, K, dtype=u8), t("sa", 1, M, 4, dtype=u8), t("qw", N, K, dtype=u8),
+                        t("sw", 1, N, 4, dtype=u8), y=t("y", M, N, dtype=bf), ws=ws)
+    elif call == "kv_scales":
+        fp8.fp8_kv_channel_scales(t("kv", M, K), "e5m2", scales=t("scales", K), ws=ws)
+    elif call == "calibrate":
+        fp8.fp8_calibrate_percentile(t("x", M, K), 999, 1000, value=t("value", 1), scale=t("scale", 1), ws=ws)
+    else:
+        raise ValueError(call)
+
+
+BINDING_TENSORS = {
+    "fused": ["x", "qw", "s_ch", "y", "qa_out", "s_tok_out", "ws"],
+    "gemm": ["qa", "s_tok", "qw", "s_ch", "y", "ws"],
+    "fp8out": ["qa", "s_tok", "qw", "s_ch", "q_out", "s_out", "y32_out", "ws"],
+    "grouped": ["qa", "s_tok", "row_token", "expert_offsets", "qw", "s_ch", "y", "ws"],
+    "quantize": ["x", "q", "scales"],
+    "gemm_mx": ["qa", "sa", "qw", "sw", "y", "ws"],
+    "kv_scales": ["kv", "scales", "ws"],
+    "calibrate": ["x", "value", "scale", "ws"],
+}
+
+
+@pytest.mark.parametrize("call,host", [(c, h) for c, hs in BINDING_TENSORS.items() for h in hs])
+def test_every_tensor_argument_must_be_on_the_device(monkeypatch, call, host):
+    """Each tensor argument of each binding, optional outputs and the
+    workspace included, is rejected when it alone is a host tensor: the C ABI
+    cannot tell a host pointer from a device pointer, and a kernel would fault
+    on the host address.  With every tensor on the 'device' the call goes on to
+    the library (the guard raises), so the rejection is the host tensor's."""
+    monkeypatch.setattr(fp8, "lib", lambda real=fp8.lib(): _GuardLib(real))
+    monkeypatch.setattr(fp8, "_stream", lambda stream: S0)
+    with pytest.raises(AssertionError, match="reached the library"):
+        _binding_case(call, None)
+    with pytest.raises((TypeError, ValueError)):
+        _binding_case(call, host)
+
+
+def test_invalid_sizes_raise_instead_of_allocating(monkeypatch):
+    """A size query answering SIZE_MAX (invalid sizes) raises the library's
+    invalid-argument error instead of asking torch for SIZE_MAX bytes."""
+    with pytest.raises(fp8.Fp8Error) as e:
+        fp8._workspace(None, fp8.SIZE_MAX, "fp8_gemm_scaled", "cpu")
+    assert e.value.code == FP8_ERR_INVALID_ARGUMENT

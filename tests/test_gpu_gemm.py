@@ -188,18 +188,39 @@ def test_repeatable_bits():
 
 # ---------------------------------------------------------------- workloads --
 
+def _tile_samples(row0, rows, N, rng, per_tile=2, tile=256):
+    """per_tile random elements inside every tile x tile block of the output
+    rows [row0, row0 + rows) x columns [0, N) (blocks clipped at the edges),
+    so that no output tile of any kernel (256 x 256 or smaller) goes unchecked."""
+    ms, ns = [], []
+    for r in range(0, rows, tile):
+        h = min(tile, rows - r)
+        for c in range(0, N, tile):
+            wd = min(tile, N - c)
+            ms.append(row0 + r + rng.integers(0, h, per_tile))
+            ns.append(c + rng.integers(0, wd, per_tile))
+    if not ms:
+        return np.zeros(0, np.int64), np.zeros(0, np.int64)
+    return np.concatenate(ms), np.concatenate(ns)
+
+
 def _sample_pairs(M, N, count, rng):
-    ms = np.concatenate([rng.integers(0, M, count), np.full(N, 0), np.full(N, M - 1), np.arange(M)])
-    ns = np.concatenate([rng.integers(0, N, count), np.arange(N), np.arange(N), np.full(M, rng.integers(0, N))])
+    """count random elements, the first and last rows and one column in full,
+    and two random elements of every 256 x 256 output tile."""
+    tm, tn = _tile_samples(0, M, N, rng)
+    ms = np.concatenate([rng.integers(0, M, count), np.full(N, 0), np.full(N, M - 1), np.arange(M), tm])
+    ns = np.concatenate([rng.integers(0, N, count), np.arange(N), np.arange(N), np.full(M, rng.integers(0, N)), tn])
     return ms, ns
 
 
 @pytest.mark.parametrize("name", ["tiny", "llama3-8b-decode-up", "llama3-70b-decode-gateup",
-                                  "llama3-70b-decode-down", "llama3-70b-prefill"])
+                                  "llama3-70b-decode-down", "llama3-70b-tp4-gateup", "llama3-70b-tp4-down",
+                                  "llama3-70b-prefill"])
 def test_workload_fused(name):
     """Full-size workloads through the fused call (the path the benchmark times):
     codes and scales bit exact on every element, outputs on sampled elements
-    (two full rows, one full column, 4096 random), full compare for the tiny one."""
+    (two full rows, one full column, 4096 random, two in every 256 x 256
+    output tile), full compare for the tiny one."""
     w = synth.WORKLOADS[name]
     M, N, K = w["M"], w["N"], w["K"]
     log(f"workload {name}: M={M} N={N} K={K}")
@@ -322,9 +343,11 @@ def test_grouped_moe_workload():
     y = to_host(fp8.fp8_gemm_grouped_scaled(qa_d, st_d, to_dev(rt), to_dev(off), qw_d, sc_d))
     R = rt.size
     rng = np.random.default_rng(0)
-    # every expert's first and last routed row in full, plus random elements
+    # every expert's first and last routed row in full, random elements, and
+    # two elements in every 256-row x 256-column output tile of every expert
     rows = np.unique(np.concatenate([off[:-1][np.diff(off) > 0], off[1:][np.diff(off) > 0] - 1]))
-    rs = np.concatenate([np.repeat(rows, N), rng.integers(0, R, 8192)])
-    ns = np.concatenate([np.tile(np.arange(N), rows.size), rng.integers(0, N, 8192)])
+    tiles = [_tile_samples(int(off[e]), int(off[e + 1] - off[e]), N, rng) for e in range(E)]
+    rs = np.concatenate([np.repeat(rows, N), rng.integers(0, R, 8192)] + [t[0] for t in tiles])
+    ns = np.concatenate([np.tile(np.arange(N), rows.size), rng.integers(0, N, 8192)] + [t[1] for t in tiles])
     ref, ab = oracle.grouped_ref_sampled(qa, st, rt, off, qw, sc, rs, ns)
     assert_within_tolerance(y[rs, ns], ref, ab, "moe sampled")

@@ -200,7 +200,7 @@ def test_16bit_kv_rows_in_and_read_back_out(fmt, fid, dtype):
     if dtype == torch.bfloat16:
         want = oracle.bf16_from_double(back32.astype(np.float64))
     else:
-        want = back32.astype(np.float16).view(np.uint16)
+        want = oracle.fp16_from_double(back32.astype(np.float64))
     assert np.array_equal(got, want), f"{fmt} {dtype} read back"
 
 

@@ -59,6 +59,7 @@ def test_zero_k_gives_floor_scales_and_empty_rows_are_a_noop():
 
 
 DENSE = ["tiny", "llama3-8b-decode-up", "llama3-70b-decode-gateup", "llama3-70b-decode-down",
+         "llama3-70b-tp4-gateup", "llama3-70b-tp4-down",
          "llama3-70b-prefill"]
 
 

@@ -61,3 +61,55 @@ def test_planted_wrong_row_scale_is_caught():
     y32, _, s = oracle.fp8out_ref(qa, s_tok, qw, s_ch)
     wrong = np.abs(y32).max(axis=0)[:M] / np.float32(448.0)
     assert not np.array_equal(s, wrong.astype(np.float32))
+
+
+def _fp8out_case(M=12, N=256, K=512, seed=5):
+    import synth
+    x, _ = synth.activations(M, K, 5, 50.0, seed=seed)
+    w = synth.weights(N, K, seed=seed)
+    qa, st = oracle.quantize_rows(x)
+    qw, sc = oracle.quantize_rows(w)
+    ref, ab = oracle.gemm_ref(qa, st, qw, sc)
+    return qa, st, qw, sc, ref, ab
+
+
+def test_admissibility_rule_accepts_every_y32_within_the_bound():
+    """The rule the GPU FP8-output test applies (tests/_helpers.py
+    fp8out_admissible) accepts the oracle's own codes and scales, and the
+    quantization of any fp32 output pushed to +-0.99 of the GEMM bound."""
+    from tests._helpers import fp8out_admissible
+    qa, st, qw, sc, ref, ab = _fp8out_case()
+    _, q, s = oracle.fp8out_ref(qa, st, qw, sc)
+    r = fp8out_admissible(q, s, ref, ab)
+    assert r["scale_ok"].all() and r["code_ok"].all()
+    b = 1e-3 * ab + 2.0 ** -22 * np.abs(ref)
+    rng = np.random.default_rng(1)
+    for sign in (+1.0, -1.0, None):
+        d = rng.choice([-1.0, 1.0], ref.shape) if sign is None else sign
+        y = (ref + 0.99 * d * b).astype(np.float32)
+        q2, s2 = oracle.quantize_rows(y)
+        r2 = fp8out_admissible(q2, s2, ref, ab)
+        assert r2["scale_ok"].all() and r2["code_ok"].all()
+        # every code that moved sits where the interval holds a rounding boundary
+        assert not np.any((q2 != q) & (s2 == s)[:, None] & ~r2["code_ambiguous"])
+
+
+def test_admissibility_rule_catches_planted_mistakes():
+    """A code moved one step where no rounding boundary is in reach, a doubled
+    row scale and a sign flip are rejected."""
+    from tests._helpers import fp8out_admissible
+    qa, st, qw, sc, ref, ab = _fp8out_case()
+    _, q, s = oracle.fp8out_ref(qa, st, qw, sc)
+    r = fp8out_admissible(q, s, ref, ab)
+    i, j = np.argwhere(~r["code_ambiguous"] & ((q & 0x7F) > 8) & ((q & 0x7F) < 0x7E))[0]
+    bad = q.copy()
+    bad[i, j] += 1
+    assert not fp8out_admissible(bad, s, ref, ab)["code_ok"][i, j]
+    s2 = s.copy()
+    s2[3] *= np.float32(2.0)
+    assert not fp8out_admissible(q, s2, ref, ab)["scale_ok"][3]
+    flip = q.copy()
+    k = np.argwhere(np.abs(ref) > 100 * (1e-3 * ab))
+    i, j = k[0]
+    flip[i, j] ^= 0x80
+    assert not fp8out_admissible(flip, s, ref, ab)["code_ok"][i, j]

@@ -2,11 +2,11 @@
 
 Pinned against:
   - hand-worked examples (tests/golden/quant_worked_examples.txt);
-  - the Llama 3 FP8 page's §3.1 conversion snippet executed by PyTorch
-    (absmax over dim=1 / 448, clamp(min=1e-12), divide, cast to
-    float8_e4m3fn), bit for bit on codes and scales.  The quotients never
-    exceed 448.00003, inside the range where PyTorch's cast and the
-    saturating encoder agree;
+  - the per-row conversion of the Llama 3 FP8 page, §3.1, formed in numpy
+    float32 (row max |x| / 448 floored at 1e-12, IEEE quotient) with only
+    the final cast done by PyTorch's float8_e4m3fn, bit for bit on codes and
+    scales.  The quotients never exceed 448.00003, inside the range where
+    PyTorch's cast and the saturating encoder agree;
   - invariants: the absmax element of each row encodes to +-448, and no code
     is NaN (the NaN/Inf scan of the same page's §4.1).
 """
@@ -19,13 +19,18 @@ import synth
 from tests._helpers import read_quant_examples
 
 
-def _pages_snippet(x: np.ndarray):
-    """The conversion the Llama 3 FP8 page, §3.1, shows, executed in PyTorch (fp32)."""
-    w = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
-    scale = w.abs().max(dim=1, keepdim=True).values / 448.0
-    scale = torch.clamp(scale, min=1e-12)
-    q = (w / scale).to(torch.float8_e4m3fn)
-    return q.view(torch.uint8).numpy(), scale.squeeze(1).numpy()
+def _library_cast_pin(x: np.ndarray):
+    """The per-row conversion the Llama 3 FP8 page describes in §3.1 (scale =
+    row max |x| / 448 with a 1e-12 floor, codes = the E4M3 cast of x / scale),
+    formed here in numpy float32 (IEEE division, correctly rounded), with only
+    the final cast of each quotient done by PyTorch's float8_e4m3fn, the
+    library routine that page's conversion relies on."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    amax = np.abs(x).max(axis=1) if x.shape[1] else np.zeros(x.shape[0], np.float32)
+    scale = np.maximum(amax / np.float32(448.0), np.float32(1e-12)).astype(np.float32)
+    quot = (x / scale[:, None]).astype(np.float32)
+    q = torch.from_numpy(quot).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return q, scale
 
 
 @pytest.mark.parametrize("i", range(5))
@@ -55,19 +60,19 @@ def _special_rows(K):
 
 
 @pytest.mark.parametrize("K", [16, 256, 4096])
-def test_matches_pages_snippet_on_synthetic_and_special_rows(K):
+def test_matches_library_cast_on_synthetic_and_special_rows(K):
     x, _ = synth.activations(64, K, synth.n_outlier_channels(K) or 1, 50.0, seed=3)
     x = np.concatenate([x, _special_rows(K)])
     q, s = oracle.quantize_rows(x)
-    tq, ts = _pages_snippet(x)
+    tq, ts = _library_cast_pin(x)
     assert np.array_equal(s.view(np.uint32), ts.view(np.uint32))
     assert np.array_equal(q, tq)
 
 
-def test_matches_pages_snippet_on_weight_rows():
+def test_matches_library_cast_on_weight_rows():
     w = synth.weights(512, 1024, seed=5)
     q, s = oracle.quantize_rows(w)
-    tq, ts = _pages_snippet(w)
+    tq, ts = _library_cast_pin(w)
     assert np.array_equal(s.view(np.uint32), ts.view(np.uint32))
     assert np.array_equal(q, tq)
 
