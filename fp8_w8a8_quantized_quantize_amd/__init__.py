@@ -37,7 +37,7 @@ EXPORTS = ("fp8_quantize_per_token", "fp8_quantize_static", "fp8_quantize_per_to
            "fp8_gemm_grouped_scaled", "fp8_workspace_bytes", "fp8_gemm_workspace_bytes", "fp8_fp8out_workspace_bytes",
            "fp8_grouped_workspace_bytes", "fp8_quantize_mx", "fp8_gemm_mx", "fp8_mx_workspace_bytes",
            "fp8_kv_channel_scales", "fp8_kv_scales_workspace_bytes",
-           "fp8_kv_quantize_paged", "fp8_kv_dequantize_paged", "fp8_status_string")
+           "fp8_kv_quantize_paged", "fp8_kv_dequantize_paged", "fp8_stream_read", "fp8_status_string")
 
 _lib = None
 
@@ -96,6 +96,8 @@ def lib():
         L.fp8_kv_quantize_paged.argtypes = [vp, st, i64, i64, i64, vp, st, vp, vp, i64, vp]
         L.fp8_kv_dequantize_paged.restype = st
         L.fp8_kv_dequantize_paged.argtypes = [vp, i64, vp, i64, i64, vp, st, vp, st, i64, vp]
+        L.fp8_stream_read.restype = st
+        L.fp8_stream_read.argtypes = [vp, sz, ctypes.c_int32, ctypes.c_int32, vp, vp]
         L.fp8_status_string.restype = ctypes.c_char_p
         L.fp8_status_string.argtypes = [st]
         _lib = L
@@ -536,3 +538,17 @@ def fp8_gemm_grouped_scaled(qa, s_tok, row_token, expert_offsets, qw, s_ch, y=No
            lib().fp8_gemm_grouped_scaled(_ptr(qa), _ptr(s_tok), _ptr(row_token), _ptr(expert_offsets), _ptr(qw),
                                          _ptr(s_ch), _ptr(y), T, R, E, N, K, _ptr(ws), _nbytes(ws), _stream(stream)))
     return y
+
+
+def fp8_stream_read(buf, workgroups=256, nontemporal=False, sink=None, stream=None):
+    """Read every byte of the contiguous device tensor `buf` once (the HBM read
+    ceiling the decode kernels are measured against); returns the sink tensor."""
+    torch = _torch()
+    if not isinstance(buf, torch.Tensor) or not buf.is_cuda or not buf.is_contiguous():
+        raise TypeError("buf: expected a contiguous CUDA tensor")
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=buf.device)
+    _vec(sink, torch.int32, "sink", 1, buf.device)
+    _check("fp8_stream_read", lib().fp8_stream_read(_ptr(buf), _nbytes(buf), int(workgroups), int(bool(nontemporal)),
+                                                    _ptr(sink), _stream(stream)))
+    return sink

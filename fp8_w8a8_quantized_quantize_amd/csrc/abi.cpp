@@ -436,4 +436,13 @@ fp8_status_t fp8_gemm_grouped_scaled(const uint8_t* qa, const float* s_tok, cons
                                               stream));
 }
 
+fp8_status_t fp8_stream_read(const void* p, size_t bytes, int32_t workgroups, int32_t nontemporal, uint32_t* sink,
+                             hipStream_t stream) {
+    if (bytes % 16 != 0 || workgroups < 1 || workgroups > (1 << 20)) return FP8_ERR_INVALID_ARGUMENT;
+    if (bytes > 0 && (p == nullptr || sink == nullptr)) return FP8_ERR_INVALID_ARGUMENT;
+    if (bytes > 0 && (!aligned16(p) || (reinterpret_cast<uintptr_t>(sink) & 3u) != 0)) return FP8_ERR_UNSUPPORTED;
+    if (bytes == 0) return FP8_OK;
+    return from_hip(fp8k::launch_stream_read(p, bytes, workgroups, nontemporal != 0, sink, stream));
+}
+
 }  // extern "C"

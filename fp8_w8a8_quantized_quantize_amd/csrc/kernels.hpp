@@ -123,4 +123,10 @@ hipError_t launch_gemm_grouped(const uint8_t* qa, const float* s_tok, const int3
                                const int32_t* offsets, const uint8_t* qw, const float* s_ch, uint16_t* y,
                                int64_t T, int64_t R, int64_t E, int64_t N, int64_t K, hipStream_t stream);
 
+// Plain streaming read of `bytes` bytes (multiple of 16, p 16-byte aligned)
+// by about `workgroups` workgroups of 256 threads (stream_read.hip); sink: one
+// uint32 that is written only when the folded data equals a magic value.
+hipError_t launch_stream_read(const void* p, size_t bytes, int workgroups, bool nontemporal, uint32_t* sink,
+                              hipStream_t stream);
+
 }  // namespace fp8k

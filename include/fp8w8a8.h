@@ -328,6 +328,21 @@ fp8_status_t fp8_kv_dequantize_paged(const uint8_t* cache, int64_t num_slots, co
                                      int64_t T, int64_t C, const float* scales, fp8_kv_format_t fmt, void* out,
                                      fp8_kv_dtype_t out_dtype, int64_t ldo, hipStream_t stream);
 
+/*
+ * HBM read ceiling (a measurement utility beside the layer, not part of it):
+ * reads the `bytes` bytes at p once with plain 16-byte vector loads
+ * (nontemporal loads when `nontemporal` != 0) from about `workgroups`
+ * workgroups of 256 threads, each streaming a contiguous share, 8 loads in
+ * flight per thread -- the request size and depth of the decode kernels, so
+ * its rate is the weight-streaming ceiling those kernels are measured against
+ * (DeepSeek V4 950 page, §1.2: decode time is the time to move the weights).
+ * The data is folded into one 32-bit value per thread, stored to *sink only
+ * when it equals 0x9E3779B9 (so the loads cannot be dropped).  bytes % 16 ==
+ * 0, 1 <= workgroups <= 2^20, p 16-byte aligned, sink 4-byte aligned.
+ */
+fp8_status_t fp8_stream_read(const void* p, size_t bytes, int32_t workgroups, int32_t nontemporal, uint32_t* sink,
+                             hipStream_t stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* fp8_status_string(fp8_status_t status);
 

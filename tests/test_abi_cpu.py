@@ -456,3 +456,13 @@ def test_invalid_sizes_raise_instead_of_allocating(monkeypatch):
     with pytest.raises(fp8.Fp8Error) as e:
         fp8._workspace(None, fp8.SIZE_MAX, "fp8_gemm_scaled", "cpu")
     assert e.value.code == FP8_ERR_INVALID_ARGUMENT
+
+
+def test_stream_read_validation():
+    L = fp8.lib()
+    # p, bytes, workgroups, nontemporal, sink, stream
+    assert L.fp8_stream_read(P, 1000, 256, 0, Q, S0) == FP8_ERR_INVALID_ARGUMENT     # bytes % 16
+    assert L.fp8_stream_read(P, 1024, 0, 0, Q, S0) == FP8_ERR_INVALID_ARGUMENT       # no workgroups
+    assert L.fp8_stream_read(0, 1024, 256, 0, Q, S0) == FP8_ERR_INVALID_ARGUMENT
+    assert L.fp8_stream_read(MIS, 1024, 256, 0, Q, S0) == FP8_ERR_UNSUPPORTED
+    assert L.fp8_stream_read(P, 0, 256, 0, 0, S0) == FP8_OK
