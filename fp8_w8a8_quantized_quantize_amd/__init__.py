@@ -37,7 +37,8 @@ EXPORTS = ("fp8_quantize_per_token", "fp8_quantize_static", "fp8_quantize_per_to
            "fp8_gemm_grouped_scaled", "fp8_workspace_bytes", "fp8_gemm_workspace_bytes", "fp8_fp8out_workspace_bytes",
            "fp8_grouped_workspace_bytes", "fp8_quantize_mx", "fp8_gemm_mx", "fp8_mx_workspace_bytes",
            "fp8_kv_channel_scales", "fp8_kv_scales_workspace_bytes",
-           "fp8_kv_quantize_paged", "fp8_kv_dequantize_paged", "fp8_stream_read", "fp8_status_string")
+           "fp8_kv_quantize_paged", "fp8_kv_dequantize_paged", "fp8_stream_read", "fp8_quant_gemm_fused_noalloc",
+           "fp8_status_string")
 
 _lib = None
 
@@ -96,6 +97,8 @@ def lib():
         L.fp8_kv_quantize_paged.argtypes = [vp, st, i64, i64, i64, vp, st, vp, vp, i64, vp]
         L.fp8_kv_dequantize_paged.restype = st
         L.fp8_kv_dequantize_paged.argtypes = [vp, i64, vp, i64, i64, vp, st, vp, st, i64, vp]
+        L.fp8_quant_gemm_fused_noalloc.restype = st
+        L.fp8_quant_gemm_fused_noalloc.argtypes = [vp, i64, vp, i64, vp, vp, i64, i64, i64, i64, vp, vp, vp]
         L.fp8_stream_read.restype = st
         L.fp8_stream_read.argtypes = [vp, sz, ctypes.c_int32, ctypes.c_int32, vp, vp]
         L.fp8_status_string.restype = ctypes.c_char_p
@@ -477,6 +480,34 @@ def fp8_quant_gemm_fused(x, qw, s_ch, y=None, qa_out=None, s_tok_out=None, ws=No
     _check("fp8_quant_gemm_fused",
            lib().fp8_quant_gemm_fused(_ptr(x), ldx, _ptr(qw), ldw, _ptr(s_ch), _ptr(y), ldy, M, N, K,
                                       _ptr(qa_out), _ptr(s_tok_out), _ptr(ws), _nbytes(ws), _stream(stream)))
+    return y
+
+
+# size of the static device scratch array of fp8_quant_gemm_fused_noalloc
+FP8_NOALLOC_SCRATCH_BYTES = 72 << 20
+
+
+def fp8_quant_gemm_fused_noalloc(x, qw, s_ch, y, qa_out=None, s_tok_out=None, stream=None):
+    """fp8_quant_gemm_fused without a workspace: the library's static device
+    scratch array holds the staged codes and split-K partial sums, so the call
+    allocates nothing (y, and qa_out / s_tok_out when wanted, are the caller's)."""
+    torch = _torch()
+    M, K, ldx = _rows(x, torch.float32, "x")
+    dev = x.device
+    N, K2, ldw = _rows(qw, torch.uint8, "qw", dev)
+    if K2 != K:
+        raise ValueError("x and qw disagree on K")
+    _vec(s_ch, torch.float32, "s_ch", N, dev)
+    My, Ny, ldy = _rows(y, torch.bfloat16, "y", dev)
+    if (My, Ny) != (M, N):
+        raise ValueError("y: expected shape [M, N]")
+    if qa_out is not None:
+        _dense(qa_out, torch.uint8, "qa_out", (M, K), dev)
+    if s_tok_out is not None:
+        _vec(s_tok_out, torch.float32, "s_tok_out", M, dev)
+    _check("fp8_quant_gemm_fused_noalloc",
+           lib().fp8_quant_gemm_fused_noalloc(_ptr(x), ldx, _ptr(qw), ldw, _ptr(s_ch), _ptr(y), ldy, M, N, K,
+                                              _ptr(qa_out), _ptr(s_tok_out), _stream(stream)))
     return y
 
 

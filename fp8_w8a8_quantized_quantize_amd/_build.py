@@ -7,7 +7,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfp8w8a8.so")
-SOURCES = ["abi.cpp", "quantize.hip", "calibrate.hip", "kv_cache.hip", "block_scale.hip", "gemm_skinny.hip", "gemm_tiled.hip", "gemm_mfma.hip", "stream_read.hip"]
+SOURCES = ["abi.cpp", "quantize.hip", "calibrate.hip", "kv_cache.hip", "block_scale.hip", "gemm_skinny.hip", "gemm_tiled.hip", "gemm_mfma.hip", "stream_read.hip", "noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 

@@ -208,6 +208,28 @@ fp8_status_t fp8_gemm_grouped_scaled(const uint8_t* qa, const float* s_tok,
                                      int64_t T, int64_t R, int64_t E, int64_t N, int64_t K,
                                      void* ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * Allocation-free fused call, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, results and kernels as fp8_quant_gemm_fused,
+ * without ws: the scratch (staged activation codes and scales, split-K
+ * partial sums) is a static device array of FP8_NOALLOC_SCRATCH_BYTES that
+ * each GPU the library runs on holds until the process ends.  The call
+ * allocates nothing; its device address is looked up once per device on the
+ * first call there.  Limits and errors: FP8_ERR_WORKSPACE when
+ * fp8_workspace_bytes(M, N, K) exceeds FP8_NOALLOC_SCRATCH_BYTES (e.g. up to
+ * M * K ~ 72 MiB of staged codes: the 8192 x 8192 x 8192 prefill fits);
+ * FP8_ERR_INVALID_ARGUMENT when `stream` belongs to another device than the
+ * calling thread's current one; otherwise as fp8_quant_gemm_fused.  All calls
+ * on one GPU share the array (nothing in it needs to start at zero): calls
+ * that overlap on one GPU race and must be serialized by the caller.
+ */
+#define FP8_NOALLOC_SCRATCH_BYTES (72u << 20)
+fp8_status_t fp8_quant_gemm_fused_noalloc(const float* x, int64_t ldx, const uint8_t* qw, int64_t ldw,
+                                          const float* s_ch, uint16_t* y, int64_t ldy,
+                                          int64_t M, int64_t N, int64_t K,
+                                          uint8_t* qa_out, float* s_tok_out, hipStream_t stream);
+
 /* Workspace bytes fp8_gemm_scaled_fp8out needs (host only; SIZE_MAX for
  * invalid sizes). */
 size_t fp8_fp8out_workspace_bytes(int64_t M, int64_t N, int64_t K);

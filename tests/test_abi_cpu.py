@@ -458,6 +458,25 @@ def test_invalid_sizes_raise_instead_of_allocating(monkeypatch):
     assert e.value.code == FP8_ERR_INVALID_ARGUMENT
 
 
+def test_noalloc_rejects_on_the_host():
+    """The allocation-free fused call checks sizes before touching any device:
+    beyond its static scratch array it returns FP8_ERR_WORKSPACE, invalid
+    sizes FP8_ERR_INVALID_ARGUMENT."""
+    L = fp8.lib()
+    # x, ldx, qw, ldw, s_ch, y, ldy, M, N, K, qa_out, s_tok_out, stream
+    big_m = fp8.FP8_NOALLOC_SCRATCH_BYTES // 4096 + 1024
+    assert fp8.fp8_workspace_bytes(big_m, 256, 4096) > fp8.FP8_NOALLOC_SCRATCH_BYTES
+    assert L.fp8_quant_gemm_fused_noalloc(P, 4096, Q, 4096, P, P, 256, big_m, 256, 4096, 0, 0, S0) \
+        == FP8_ERR_WORKSPACE
+    assert L.fp8_quant_gemm_fused_noalloc(P, 4096, Q, 4096, P, P, 256, -1, 256, 4096, 0, 0, S0) \
+        == FP8_ERR_INVALID_ARGUMENT
+    # the prefill shape fits
+    assert fp8.fp8_workspace_bytes(8192, 8192, 8192) <= fp8.FP8_NOALLOC_SCRATCH_BYTES
+    text = open(HEADER).read()
+    assert re.search(r"#define FP8_NOALLOC_SCRATCH_BYTES \(72u << 20\)", text)
+    assert fp8.FP8_NOALLOC_SCRATCH_BYTES == 72 << 20
+
+
 def test_stream_read_validation():
     L = fp8.lib()
     # p, bytes, workgroups, nontemporal, sink, stream
