@@ -64,9 +64,10 @@ def _check_against_oracle_output(q, s, ref, absref, o_q, o_s, what, max_rate=0.0
     assert rate <= max_rate, f"{what}: {rate:.4%} of the codes differ from the oracle's FP8 output"
 
 
-# (M, N, K): skinny, skinny split-K (4 and 8 parts), MFMA (K % 128 == 0), tiled (K % 128 != 0)
+# (M, N, K): skinny, skinny split-K (4 and 8 parts), MFMA (K % 128 == 0), tiled (K % 128 != 0),
+# and a 144 MB fp32 output with a ragged last row tile
 SHAPES = [(8, 512, 1024), (16, 4096 + 32, 512), (64, 1024, 4096), (40, 1008, 8240),
-          (200, 320, 640), (300, 1024, 4096), (129, 512, 400), (513, 256, 2064)]
+          (200, 320, 640), (300, 1024, 4096), (129, 512, 400), (513, 256, 2064), (4400, 8192, 256)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
