@@ -31,8 +31,11 @@ def _check(x_np, what, ld=None):
     assert_codes_equal(q, oq, what)
 
 
+# the last two rows take the two-pass loop kernel: rows too long for registers
+# (K > 32768 with 256 threads per row, K > 65536 with 1024 for short batches)
 @pytest.mark.parametrize("rows,K,ld", [(1, 16, 16), (3, 48, 64), (77, 1040, 1040), (5, 4112, 4128),
-                                       (2, 16400, 16400), (9, 28672, 28672), (300, 256, 260)])
+                                       (2, 16400, 16400), (9, 28672, 28672), (300, 256, 260),
+                                       (600, 33024, 33040), (2, 65600, 65600)])
 def test_shapes_and_strides(rows, K, ld):
     log(f"quantize rows={rows} K={K} ld={ld}")
     x, _ = synth.activations(rows, K, max(1, synth.n_outlier_channels(K)), 50.0, seed=rows + K)
